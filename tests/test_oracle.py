@@ -1,0 +1,62 @@
+"""CPU tests of the oracle: every pin in oracle_pins.py against the oracle,
+and planted mistakes in copies of the oracle that some pin must catch."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle_pins import PINS
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name, oracle_lib):
+    PINS[name](oracle_lib)
+
+
+def test_parent_logit_recovery_exact():
+    oracle_pins.pin_parent_logit_recovery()
+
+
+# (what the mistake is, exact source text, replacement)
+MUTANTS = [
+    ("correction sign flipped",
+     "exp(s[c] - m) - exp(sp - m) : 0.0;", "exp(sp - m) - exp(s[c] - m) : 0.0;"),
+    ("parent logit is not the mean of all children", "sp /= C;", "sp /= (C + 1);"),
+    ("child comparison not strict", "if (dc < dchild) { dchild = dc; cstar = c0 + c; }",
+     "if (dc <= dchild) { dchild = dc; cstar = c0 + c; }"),
+    ("move on a tie with the parent", "(C > 0 && dchild < dbest)", "(C > 0 && dchild <= dbest)"),
+    ("last minimum among parents", "if (dm < dbest) { dbest = dm; a = m; }", "if (dm <= dbest) { dbest = dm; a = m; }"),
+    ("children of the wrong parent", "int64_t c0 = M0 + (int64_t)a * C;", "int64_t c0 = M0 + (int64_t)((a + 1) % M0) * C;"),
+    ("denominator without counts", "z += A * n[j];", "z += A;"),
+    ("empty children not masked", "double dA = n[c0 + c] > 0 ? exp(s[c] - m) - exp(sp - m) : 0.0;",
+     "double dA = exp(s[c] - m) - exp(sp - m);"),
+    ("running max over empty children", "if (n[c0 + c] > 0 && s[c] > mnew) mnew = s[c];", "if (s[c] > mnew) mnew = s[c];"),
+    ("importance without counts", "wt[j] += expf(s[j] - m) * (float)n[j] / Z;", "wt[j] += expf(s[j] - m) / Z;"),
+    ("importance without the logit scale", "s[j] = (float)scale * acc;", "s[j] = acc;"),
+    ("top-P ties to the higher index", "if (wr[jj] > wr[j] || (wr[jj] == wr[j] && jj < j)) ++ahead;",
+     "if (wr[jj] > wr[j] || (wr[jj] == wr[j] && jj > j)) ++ahead;"),
+    ("parent rows miss the moved keys", "ct[a] += 1;", "ct[a] += (r == a);"),
+    ("no residual for a refined parent", "nn[a] -= n[c0 + c];", ";"),
+    ("brute force ignores the selection", "int32_t khat = (r != a && in_sel(S, P, a)) ? r : a;",
+     "int32_t khat = r;"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(what, old, new, tmp_path):
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique: {old}"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    oracle.build(str(mpath), so)
+    lib = oracle.load(so)
+    failed = []
+    for name, pin in PINS.items():
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(name)
+    assert failed, f"no pin catches: {what}"
