@@ -1,0 +1,145 @@
+"""ctypes binding of libavq (include/avq.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of libavq.so.  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libavq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "avq.h")
+
+AVQ_F32 = 0
+AVQ_BF16 = 1
+STATUS = {0: "AVQ_OK", -1: "AVQ_ERR_NULL", -2: "AVQ_ERR_SHAPE", -3: "AVQ_ERR_DTYPE", -4: "AVQ_ERR_ALIGN",
+          -5: "AVQ_ERR_UNSUPPORTED", -6: "AVQ_ERR_HIP"}
+
+
+class AvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib.avq_status_string(status).decode() if _lib is not None else ""
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({msg})")
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libavq.so not found at {path}; build it with __graft_entry__.build() "
+                          "or python adaptive_vector_quantized_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.avq_assign_aggregate.argtypes = [P, P, P] + [i32] * 7 + [P, P, P, P]
+    lib.avq_assign_aggregate.restype = i32
+    lib.avq_attention_fwd.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P]
+    lib.avq_attention_fwd.restype = i32
+    lib.avq_status_string.argtypes = [i32]
+    lib.avq_status_string.restype = ctypes.c_char_p
+    lib.avq_version.argtypes = []
+    lib.avq_version.restype = i32
+    return lib
+
+
+_lib: Optional[ctypes.CDLL] = None
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def declared_symbols(header: str = HEADER):
+    """Names of the functions include/avq.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(avq_\w+)\s*\(", text, flags=re.M)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return AVQ_F32
+    if t.dtype == torch.bfloat16:
+        return AVQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape4(t: torch.Tensor, name: str) -> Tuple[int, int, int, int]:
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    return tuple(t.shape)
+
+
+def assign_aggregate(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C: int, *,
+                     want_assign: bool = False, vsum: Optional[torch.Tensor] = None,
+                     counts: Optional[torch.Tensor] = None, assign: Optional[torch.Tensor] = None):
+    """Kernel 1.  K, V: [B, H, N, d]; codebook: [H, M0*(1+C), d] (same dtype).
+    Returns (vsum [B, H, Mt, d] float32, counts [B, H, Mt] int32, assign [B, H, N] int32 or None)."""
+    B, H, N, d = _shape4(K, "K")
+    if tuple(V.shape) != (B, H, N, d) or V.dtype != K.dtype or not V.is_contiguous():
+        raise ValueError("V must match K")
+    if codebook.dim() != 3 or codebook.shape[0] != H or codebook.shape[2] != d or not codebook.is_contiguous():
+        raise ValueError("codebook must be a contiguous [H, Mt, d] tensor")
+    Mt = codebook.shape[1]
+    if Mt % (1 + C):
+        raise ValueError("codebook rows must be M0 * (1 + C)")
+    M0 = Mt // (1 + C)
+    dev = K.device
+    if vsum is None:
+        vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
+    if want_assign and assign is None:
+        assign = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    rc = _lib.avq_assign_aggregate(_ptr(K), _ptr(V), _ptr(codebook), B, H, N, d, M0, C, _dtype_code(K),
+                                   _ptr(vsum), _ptr(counts), _ptr(assign), _stream(K))
+    if rc != 0:
+        raise AvqError(rc, "avq_assign_aggregate")
+    return vsum, counts, assign
+
+
+def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, counts: torch.Tensor, C: int, P: int,
+                  block_q: int, scale: Optional[float] = None, *, want_topp: bool = False,
+                  want_importance: bool = False, Y: Optional[torch.Tensor] = None):
+    """Kernel 2.  Q: [B, H, N, d]; codebook [H, Mt, d]; vsum/counts from assign_aggregate.
+    Returns (Y [B, H, N, d] float32, topp [B, H, T, P] int32 or None, importance [B, H, T, M0] or None)."""
+    B, H, N, d = _shape4(Q, "Q")
+    Mt = codebook.shape[1]
+    M0 = Mt // (1 + C)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    dev = Q.device
+    T = (N + block_q - 1) // block_q
+    if Y is None:
+        Y = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    topp = torch.empty((B, H, T, P), dtype=torch.int32, device=dev) if want_topp else None
+    imp = torch.empty((B, H, T, M0), dtype=torch.float32, device=dev) if want_importance else None
+    for name, t in (("vsum", vsum), ("counts", counts)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    rc = _lib.avq_attention_fwd(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
+                                _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(imp),
+                                _stream(Q))
+    if rc != 0:
+        raise AvqError(rc, "avq_attention_fwd")
+    return Y, topp, imp
+
+
+def forward(Q, K, V, codebook, C: int, P: int, block_q: int, scale: Optional[float] = None):
+    """The whole AVQ-Attention forward pass: kernel 1 then kernel 2 on the current stream."""
+    vsum, counts, _ = assign_aggregate(K, V, codebook, C)
+    Y, _, _ = attention_fwd(Q, codebook, vsum, counts, C, P, block_q, scale)
+    return Y

@@ -1,0 +1,48 @@
+"""Build libavq.so (the HIP kernels and the C interface) for gfx950 with hipcc.
+
+The library is built in-tree next to this file so that it travels with the
+source tree; the Python binding loads it from there.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libavq.so")
+SOURCES = ["api.hip", "assign_aggregate.hip", "attention.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-munsafe-fp-atomics",
+    # no packed fp32 instructions anywhere in the library
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    return cand if os.path.exists(cand) else "hipcc"
+
+
+def build(out: str = LIB, extra=()) -> str:
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if msgs.strip():
+        print(msgs, file=sys.stderr)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

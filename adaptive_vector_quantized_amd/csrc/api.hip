@@ -1,0 +1,86 @@
+// C interface of libavq: argument validation on the host, then the launches.
+// The contract of every entry point is documented in include/avq.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/avq.h"
+#include "avq_launch.h"
+
+namespace {
+
+constexpr int kAssignChunk = 512;    // keys per workgroup of the assignment kernel
+constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(int B, int H, int N, int d, int M0, int C, int dtype) {
+  if (dtype != AVQ_F32 && dtype != AVQ_BF16) return AVQ_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0) return AVQ_ERR_SHAPE;
+  if (d < 1 || M0 < 1 || C < 1) return AVQ_ERR_SHAPE;
+  if (d != 64 && d != 128) return AVQ_ERR_UNSUPPORTED;
+  if (M0 > 256 || C > 16) return AVQ_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > 65535) return AVQ_ERR_UNSUPPORTED;
+  return AVQ_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? AVQ_OK : AVQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int avq_assign_aggregate(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0, int C,
+                         int dtype, float* vsum, int32_t* counts, int32_t* assign, void* stream) {
+  int rc = check_common(B, H, N, d, M0, C, dtype);
+  if (rc != AVQ_OK) return rc;
+  const int64_t BH = (int64_t)B * H;
+  if (BH == 0) return AVQ_OK;
+  if (!vsum || !counts || !codebook) return AVQ_ERR_NULL;
+  if (N > 0 && (!K || !V)) return AVQ_ERR_NULL;
+  if (!aligned16(vsum) || !aligned16(counts) || !aligned16(codebook) || (K && !aligned16(K)) ||
+      (V && !aligned16(V)) || (assign && !aligned16(assign)))
+    return AVQ_ERR_ALIGN;
+  if (avq::assign_smem_bytes(dtype, d, M0, C, kAssignChunk) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
+  const int64_t Mt = (int64_t)M0 * (1 + C);
+  hipStream_t st = (hipStream_t)stream;
+  rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, counts, BH * Mt, st));
+  if (rc != AVQ_OK || N == 0) return rc;
+  return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, kAssignChunk, vsum, counts,
+                                     assign, st));
+}
+
+int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H,
+                      int N, int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y,
+                      int32_t* topp, float* importance, void* stream) {
+  int rc = check_common(B, H, N, d, M0, C, dtype);
+  if (rc != AVQ_OK) return rc;
+  if (P < 0 || P > M0) return AVQ_ERR_SHAPE;
+  if (block_q != 32 && block_q != 64 && block_q != 128) return AVQ_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return AVQ_ERR_SHAPE;
+  const int64_t BH = (int64_t)B * H;
+  if (BH == 0 || N == 0) return AVQ_OK;
+  if (!Q || !codebook || !vsum || !counts || !Y) return AVQ_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(codebook) || !aligned16(vsum) || !aligned16(counts) || !aligned16(Y) ||
+      (topp && !aligned16(topp)) || (importance && !aligned16(importance)))
+    return AVQ_ERR_ALIGN;
+  if (avq::attention_smem_bytes(dtype, d, M0, P, block_q) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
+  return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
+                                        Y, topp, importance, (hipStream_t)stream));
+}
+
+const char* avq_status_string(int status) {
+  switch (status) {
+    case AVQ_OK: return "ok";
+    case AVQ_ERR_NULL: return "a required pointer is NULL";
+    case AVQ_ERR_SHAPE: return "a size is out of range";
+    case AVQ_ERR_DTYPE: return "unknown dtype";
+    case AVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case AVQ_ERR_UNSUPPORTED: return "unsupported size (d, M0, C, block_q or B*H)";
+    case AVQ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int avq_version(void) { return 100; }
+
+}  // extern "C"

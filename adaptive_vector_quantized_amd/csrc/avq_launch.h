@@ -1,0 +1,20 @@
+// Host-side launchers of the AVQ kernels (internal to libavq).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace avq {
+
+size_t assign_smem_bytes(int dtype, int d, int M0, int C, int chunk);
+size_t attention_smem_bytes(int dtype, int d, int M0, int P, int block_q);
+
+hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st);
+hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
+                         int C, int chunk, float* vsum, int* counts, int* assign, hipStream_t st);
+hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
+                            int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
+                            float* importance, hipStream_t st);
+
+}  // namespace avq

@@ -1,0 +1,145 @@
+/*
+ * avq.h -- C interface of libavq, the AVQ-Attention forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: "AVQ-Attention: Adaptive Vector-Quantized Attention" (arXiv
+ * 2607.12789v1).  The forward pass is two calls:
+ *
+ *   avq_assign_aggregate   the VQ precompute of Sec. 4.2 / Algorithm 1:
+ *                          two-level assignment of every key and the per-
+ *                          codeword value sums and key counts of Eq. 3.
+ *   avq_attention_fwd      the attention of Sec. 4.3 / Algorithm 2: count-
+ *                          weighted attention over the parents (Eq. 6), the
+ *                          per-query-tile importance (Eq. 7), top-P parent
+ *                          selection, and the child correction (Eq. 8, Eq. 9).
+ *
+ * Conventions shared by both calls
+ * --------------------------------
+ * Pointers are device pointers (memory from hipMalloc or any allocator that
+ * returns device memory), owned by the caller.  The library allocates no
+ * device or host memory, keeps no state between calls and is safe to call
+ * from several host threads.  Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL is the default stream).
+ *
+ * Shapes (all row-major and contiguous):
+ *   bh = b*H + h indexes (batch, head); BH = B*H.
+ *   Mt = M0 * (1 + C) codewords per head: rows 0..M0-1 are the parents; the C
+ *   children of parent m are rows M0 + m*C ... M0 + m*C + C - 1 (Alg. 1 input
+ *   layout).  The codebook is per head and shared across the batch.
+ *   Each parent must equal the mean of its C children (Sec. 4.1, Eq. 5).  If
+ *   it does not, avq_attention_fwd still returns Algorithm 2's value, but that
+ *   value no longer equals attention over the refined codebook.
+ *
+ * dtype: AVQ_F32 (float) or AVQ_BF16 (bfloat16) for Q, K, V and the codebook.
+ * Value sums, counts and outputs are float / int32 in both cases.
+ *
+ * Supported sizes: d in {64, 128}; 1 <= M0 <= 256; 1 <= C <= 16;
+ * B, H, N >= 0 (any of them zero makes the call a no-op, except that
+ * avq_assign_aggregate still zeroes vsum and counts when B*H > 0).
+ * Every pointer argument must be 16-byte aligned.
+ *
+ * Errors: every call returns AVQ_OK (0) or a negative status.  Arguments are
+ * validated on the host before anything is launched; on a validation error
+ * nothing is written.  A launch failure returns AVQ_ERR_HIP; faults that occur
+ * while a kernel runs surface at the caller's next synchronisation.
+ */
+#ifndef AVQ_H
+#define AVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AVQ_OK 0
+#define AVQ_ERR_NULL (-1)        /* a required pointer is NULL */
+#define AVQ_ERR_SHAPE (-2)       /* a size is out of range */
+#define AVQ_ERR_DTYPE (-3)       /* unknown dtype */
+#define AVQ_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
+#define AVQ_ERR_UNSUPPORTED (-5) /* valid but unsupported (d, M0, C, block_q) */
+#define AVQ_ERR_HIP (-6)         /* the HIP runtime reported an error */
+
+#define AVQ_F32 0
+#define AVQ_BF16 1
+
+/*
+ * Two-level VQ assignment and aggregation (Sec. 4.2, Algorithm 1; Eq. 2, 3).
+ *
+ * For every key of every (batch, head): the nearest parent by squared
+ * Euclidean distance (lowest index on equal distances), then the C children
+ * of that parent in order, keeping a child only if strictly closer than the
+ * best child so far; the key moves to that child only if it is strictly
+ * closer than the parent.  Every key adds its value and a count of one to
+ * its parent row (a parent row holds its whole cluster); a key that moved also
+ * adds them to its child row.
+ *
+ *   K, V      in  [BH, N, d]  dtype
+ *   codebook  in  [H, Mt, d]  dtype
+ *   vsum      out [BH, Mt, d] float   value sums (zeroed by the call first)
+ *   counts    out [BH, Mt]    int32   key counts (zeroed by the call first)
+ *   assign    out [BH, N]     int32   final row of every key (its child row
+ *                                     if it moved, else its parent row), or
+ *                                     NULL to skip
+ *
+ * Value sums are accumulated with floating-point atomics, so their rounding
+ * depends on the order keys are added in; counts and assignments are exact.
+ */
+int avq_assign_aggregate(const void* K, const void* V, const void* codebook,
+                         int B, int H, int N, int d, int M0, int C, int dtype,
+                         float* vsum, int32_t* counts, int32_t* assign,
+                         void* stream);
+
+/*
+ * AVQ attention forward (Sec. 4.3, Algorithm 2; Eq. 6-9, Sec. C and D).
+ *
+ * Queries are processed in tiles of block_q consecutive tokens (the last tile
+ * may be partial); the tile is the unit of parent selection.  For each tile:
+ *   s_ij = scale * Q_i . C_j for the parents j; m_i = max over parents with
+ *   n_j > 0 (Eq. 18); A_ij = exp(s_ij - m_i), zero where n_j = 0;
+ *   X_i = sum_j A_ij Vsum_j, Z_i = sum_j A_ij n_j (Eq. 6);
+ *   w_j = sum_{i in tile} A_ij n_j / Z_i (Eq. 7);
+ *   the P parents of largest w (ties to the lower index) are refined: for
+ *   their children c, s_ic = scale * Q_i . C_c, the running max is merged,
+ *   s_ip = mean over the C children of s_ic (Eq. 8, needs Eq. 5),
+ *   dA_ic = exp(s_ic - m_i) - exp(s_ip - m_i), zero where n_c = 0 (Eq. 9,
+ *   Sec. D), X_i += sum_c dA_ic Vsum_c, Z_i += sum_c dA_ic n_c;
+ *   Y_i = X_i / Z_i.
+ * When M0 > 64 the parents are processed in tiles of 64 and the exact
+ * denominator Z_i is completed in a first pass before the importances are
+ * formed in a second pass.
+ *
+ *   Q          in  [BH, N, d]  dtype
+ *   codebook   in  [H, Mt, d]  dtype
+ *   vsum       in  [BH, Mt, d] float  (from avq_assign_aggregate)
+ *   counts     in  [BH, Mt]    int32  (from avq_assign_aggregate)
+ *   P          0 <= P <= M0 (P = 0: plain VQ attention over the parents)
+ *   block_q    query tile: 32, 64 or 128 (one wave of 64 lanes per 32 queries)
+ *   scale      logit scale (1/sqrt(d) in the usual convention, Sec. 3.1)
+ *   Y          out [BH, N, d] float
+ *   topp       out [BH, ceil(N/block_q), P] int32, the selected parents of
+ *              each tile in ascending order, or NULL to skip
+ *   importance out [BH, ceil(N/block_q), M0] float, w_j per tile, or NULL
+ *
+ * Precision (bf16 inputs): logits use bf16 inputs with float accumulation;
+ * the weighted value sums use fp16 operands (weights in [-1, 1], value sums
+ * scaled by a power of two per codeword chunk) with float accumulation;
+ * softmax bookkeeping, denominators and importances are float.  fp32 inputs
+ * use float throughout.
+ */
+int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum,
+                      const int32_t* counts, int B, int H, int N, int d, int M0,
+                      int C, int dtype, int P, int block_q, float scale,
+                      float* Y, int32_t* topp, float* importance, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* avq_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int avq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AVQ_H */

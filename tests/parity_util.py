@@ -1,0 +1,90 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C
+interface and the oracle on the same generator arrays, and compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from adaptive_vector_quantized_amd import gen
+
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(a: np.ndarray, dtype: str, B: int, H: int):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    t = t.reshape((B, H) + tuple(a.shape[1:])) if a.shape[0] == B * H else t
+    return t.contiguous().cuda()
+
+
+def run_gpu(data: dict, P: int, want_assign=True, want_topp=True, want_importance=True, bq=None):
+    """Both kernels through the C interface; returns numpy arrays shaped like the oracle's."""
+    import torch
+    from adaptive_vector_quantized_amd import _lib
+    cfg = data["cfg"]
+    B, H = cfg.B, cfg.H
+    bq = bq or cfg.block_q
+    K = to_device(data["K"], cfg.dtype, B, H)
+    V = to_device(data["V"], cfg.dtype, B, H)
+    Q = to_device(data["Q"], cfg.dtype, B, H)
+    cb = torch.from_numpy(data["codebook"])
+    cb = (cb.to(torch.bfloat16) if cfg.dtype == "bf16" else cb).contiguous().cuda()
+    vsum, counts, assign = _lib.assign_aggregate(K, V, cb, cfg.C, want_assign=want_assign)
+    Y, topp, imp = _lib.attention_fwd(Q, cb, vsum, counts, cfg.C, P, bq, cfg.scale,
+                                      want_topp=want_topp and P > 0, want_importance=want_importance)
+    torch.cuda.synchronize()
+    BH = B * H
+    out = {
+        "vsum": vsum.cpu().numpy().reshape(BH, cfg.Mt, cfg.d),
+        "counts": counts.cpu().numpy().reshape(BH, cfg.Mt),
+        "Y": Y.cpu().numpy().reshape(BH, cfg.N, cfg.d),
+    }
+    if assign is not None:
+        out["row"] = assign.cpu().numpy().reshape(BH, cfg.N)
+    if topp is not None:
+        out["sel"] = topp.cpu().numpy().reshape(BH, -1, P)
+    if imp is not None:
+        out["importance"] = imp.cpu().numpy().reshape(BH, -1, cfg.M0)
+    return out
+
+
+def y_tolerance(dtype: str) -> float:
+    """Max-abs error allowed on the attention output, relative to its max-abs value."""
+    return 1e-5 if dtype == "f32" else 2e-3
+
+
+def check_vsum(g_vsum, o_vsum, o_abs, counts):
+    """Float32 sums of n terms in any order: |error| <= gamma_n * sum|v| (the
+    standard bound for recursive summation; the oracle sums in double)."""
+    n = counts.astype(np.float64)[..., None]
+    gamma = n * U32 / np.maximum(1.0 - n * U32, 1e-300)
+    err = np.abs(g_vsum.astype(np.float64) - o_vsum)
+    bound = gamma * o_abs + 1e-30
+    bad = err > bound
+    assert not bad.any(), f"value sums outside the float32 summation bound at {np.argwhere(bad)[:5]}"
+
+
+def compare_y(g_Y, o_Y, dtype: str, where=""):
+    scale = np.abs(o_Y).max()
+    err = np.abs(g_Y.astype(np.float64) - o_Y).max()
+    tol = y_tolerance(dtype)
+    say(f"  Y {where}: max|err|/max|Y| = {err / scale:.3e} (tol {tol:g})")
+    assert err <= tol * scale, f"Y mismatch {where}: {err / scale:.3e} > {tol:g}"
+    return err / scale
+
+
+def sub_problem(data: dict, bh: int, t: int):
+    """Queries of one tile of one (batch, head) as a stand-alone problem for the
+    oracle's per-tile steps (importance, selection, output)."""
+    cfg = data["cfg"]
+    i0, i1 = t * cfg.block_q, min(cfg.N, (t + 1) * cfg.block_q)
+    return data["Q"][bh:bh + 1, i0:i1], i0, i1

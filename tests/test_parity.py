@@ -1,0 +1,124 @@
+"""GPU parity: the HIP path (through the C interface) against the CPU oracle on
+the same seeded generator arrays.
+
+Bar: assignments, counts and top-P sets bit-exact; value sums within the
+float32 summation bound; importances within 1e-5 * |tile| of the oracle;
+outputs within 1e-5 * max|Y| (fp32 inputs) or 2e-3 * max|Y| (bf16 inputs)
+of the substituted-codebook form of the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from adaptive_vector_quantized_amd import gen
+from parity_util import check_vsum, compare_y, run_gpu, say, sub_problem
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def _data(name, seed=None, **over):
+    key = (name, seed, tuple(sorted(over.items())))
+    if key not in _cache:
+        cfg = gen.CONFIGS[name].replace(**over)
+        _cache[key] = gen.make(cfg, seed=seed, checker=oracle.MarginChecker())
+    return _cache[key]
+
+
+def _full_check(data, P, bq=None):
+    cfg = data["cfg"]
+    bq = bq or cfg.block_q
+    say(f"[parity] {cfg.name} B{cfg.B} H{cfg.H} N{cfg.N} d{cfg.d} M0{cfg.M0} C{cfg.C} P{P} bq{bq} {cfg.dtype} seed {cfg.seed}")
+    g = run_gpu(data, P, bq=bq)
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(g["row"], row), f"assignments differ at {np.argwhere(g['row'] != row)[:5]}"
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    assert np.array_equal(g["counts"], counts), "counts differ"
+    vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
+    check_vsum(g["vsum"], vsum, vabs, counts)
+    w = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    w64 = o.importance_f64(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    werr = np.abs(g["importance"].astype(np.float64) - w64).max()
+    say(f"  importance max|err| = {werr:.3e}")
+    assert werr <= 1e-5 * bq
+    if P > 0:
+        sel = o.select(w, P)
+        assert np.array_equal(g["sel"], sel), f"top-P differs at {np.argwhere((g['sel'] != sel).any(-1))[:5]}"
+    else:
+        sel = np.zeros((cfg.BH, (cfg.N + bq - 1) // bq, 0), np.int32)
+    Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel, P, bq, cfg.scale)
+    compare_y(g["Y"], Y, cfg.dtype, f"{cfg.name} P={P}")
+
+
+@pytest.mark.parametrize("seed", [1000, 1, 2, 3])
+def test_tiny_fp32(seed):
+    _full_check(_data("tiny", seed=seed), gen.CONFIGS["tiny"].P)
+
+
+@pytest.mark.parametrize("P", [0, 1, 4, 16])
+def test_tiny_fp32_P(P):
+    _full_check(_data("tiny"), P)
+
+
+def test_tiny_ragged_tail():
+    # N not a multiple of the query tile or of the key chunk
+    _full_check(_data("tiny", N=1000), 4)
+
+
+def test_tiny_bf16():
+    _full_check(_data("tiny", dtype="bf16"), 4)
+
+
+@pytest.mark.parametrize("seed", [1001, 5])
+def test_grid64(seed):
+    _full_check(_data("grid64", seed=seed), 16)
+
+
+@pytest.mark.parametrize("bq", [32, 128])
+def test_grid64_block_q(bq):
+    _full_check(_data("grid64", block_q=bq), 16)
+
+
+def test_grid64_d128():
+    _full_check(_data("grid64", d=128, H=2), 16)
+
+
+@pytest.mark.parametrize("C", [1, 3, 5, 16])
+def test_child_widths(C):
+    _full_check(_data("grid64", C=C, H=2, N=1024 + 37, grid=None), 8)
+
+
+@pytest.mark.parametrize("M0,P", [(100, 20), (256, 32), (200, 0)])
+def test_tiled_parents(M0, P):
+    # parents beyond one tile of 64: exact two-pass denominator
+    _full_check(_data("grid64", M0=M0, H=2, N=2048 + 64 + 5, grid=None), P)
+
+
+def test_full_size_grid128():
+    """The headline workload at full size: every assignment, count and value
+    sum, plus sampled query tiles for importance, top-P and output."""
+    data = _data("grid128")
+    cfg = data["cfg"]
+    say(f"[parity] grid128 full size B{cfg.B} H{cfg.H} N{cfg.N}")
+    g = run_gpu(data, cfg.P)
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(g["row"], row)
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    assert np.array_equal(g["counts"], counts)
+    vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
+    check_vsum(g["vsum"], vsum, vabs, counts)
+    rng = np.random.default_rng(7)
+    picks = [(int(rng.integers(cfg.BH)), int(rng.integers(cfg.tiles))) for _ in range(48)] + [(cfg.BH - 1, cfg.tiles - 1)]
+    for bh, t in picks:
+        h = bh % cfg.H
+        Qt, i0, i1 = sub_problem(data, bh, t)
+        os_ = oracle.Oracle(1, 1, i1 - i0, cfg.d, cfg.M0, cfg.C)
+        cbh = data["codebook"][h:h + 1]
+        w = os_.importance(Qt, cbh, counts[bh:bh + 1], cfg.block_q, cfg.scale)
+        sel = os_.select(w, cfg.P)
+        assert np.array_equal(g["sel"][bh, t], sel[0, 0]), (bh, t)
+        Y = os_.attention_substituted(Qt, cbh, vsum[bh:bh + 1], counts[bh:bh + 1], sel, cfg.P, cfg.block_q, cfg.scale)
+        compare_y(g["Y"][bh:bh + 1, i0:i1], Y, cfg.dtype, f"grid128 bh{bh} tile{t}")
