@@ -3,6 +3,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "../../include/avq.h"
 #include "avq_launch.h"
 
@@ -26,6 +29,22 @@ int check_common(int B, int H, int N, int d, int M0, int C, int dtype) {
 int from_hip(hipError_t e) { return e == hipSuccess ? AVQ_OK : AVQ_ERR_HIP; }
 
 }  // namespace
+
+namespace avq {
+
+hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  static std::mutex mu;
+  static std::unordered_map<const void*, size_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = done.find(kernel);
+  if (it != done.end() && it->second >= bytes) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[kernel] = bytes;
+  return e;
+}
+
+}  // namespace avq
 
 extern "C" {
 

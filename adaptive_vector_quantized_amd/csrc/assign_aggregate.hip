@@ -377,7 +377,7 @@ static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, 
                                   int chunk, float* vsum, int* counts, int* assign, hipStream_t st) {
   const size_t smem = assign_smem_bytes(std::is_same<T, TF32>::value ? 0 : 1, D, M0, C, chunk);
   auto kern = assign_aggregate_kernel<T, D, W>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t e = raise_lds_limit((const void*)kern, smem);
   if (e != hipSuccess) return e;
   dim3 grid((N + chunk - 1) / chunk, BH);
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, (const typename T::in_t*)K, (const typename T::in_t*)V,

@@ -413,7 +413,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
                                 hipStream_t st) {
   const size_t smem = attention_smem_bytes(std::is_same<T, TF32>::value ? 0 : 1, D, M0, P, bq);
   auto kern = attention_kernel<T, D, W>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t e = raise_lds_limit((const void*)kern, smem);
   if (e != hipSuccess) return e;
   dim3 grid((N + bq - 1) / bq, BH);
   const float sl2 = scale * 1.4426950408889634f;

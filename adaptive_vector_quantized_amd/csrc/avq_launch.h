@@ -7,6 +7,11 @@
 
 namespace avq {
 
+// Raise a kernel's dynamic-LDS limit when a launch needs more than the
+// default; remembers the largest size set per kernel so the attribute call is
+// made once per size class, not on every launch.
+hipError_t raise_lds_limit(const void* kernel, size_t bytes);
+
 size_t assign_smem_bytes(int dtype, int d, int M0, int C, int chunk);
 size_t attention_smem_bytes(int dtype, int d, int M0, int P, int block_q);
 

@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the AVQ-Attention forward pass on one MI355X.
+
+One step = one pass of the whole hot path over one batch: kernel 1
+(avq_assign_aggregate: zero fill + two-level assignment + value sums and
+counts) then kernel 2 (avq_attention_fwd: parent attention, importance, top-P,
+child correction, output), both through the C interface, on synthetic inputs
+already resident in HBM.  Three input sets are rotated (larger than the
+256 MB Infinity Cache together) so that every step streams from HBM.
+
+Prints one JSON line:
+  value            tokens per second of the whole pass, in millions (B*N / step time)
+  roofline         the dominant kernel's algorithmic bytes per launch over its
+                   average duration (HIP events on the launch stream, inside the
+                   timed region) against MI355X's 8 TB/s HBM peak
+  kernels          the same figures for both kernels, with MFMA fractions
+  cpu_baseline     the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grid128]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "AVQ fwd Mtokens/s at N=16384,H=16,d=64,M0=64,C=8,P=16; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP32_PEAK_TFLOPS = 157.3
+KERNEL_SOURCES = {
+    "assign_aggregate_kernel": ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
+                                "adaptive_vector_quantized_amd/csrc/avq_device.h"],
+    "attention_kernel": ["adaptive_vector_quantized_amd/csrc/attention.hip",
+                         "adaptive_vector_quantized_amd/csrc/avq_device.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(cfg, P):
+    """Bytes each kernel must move and flops it must do, per launch.
+
+    Kernel 1: read K and V once, the head codebooks once, write the value sums
+    and counts once; flops 2 d (M0 + C) per key (parent and child distances).
+    Kernel 2: read Q once, write Y (float32) once, read codebooks, value sums
+    and counts once; MFMA flops 4 d (M0 + P C) per query (logits and weighted
+    value sums over the M0 + P C codewords a tile uses)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    BH, N, d, M0, C, Mt = cfg.BH, cfg.N, cfg.d, cfg.M0, cfg.C, cfg.Mt
+    cb = cfg.H * Mt * d * es
+    aggr = BH * Mt * (d * 4 + 4)
+    k1_bytes = 2 * BH * N * d * es + cb + aggr
+    k2_bytes = BH * N * d * es + BH * N * d * 4 + cb + aggr
+    k1_flops = 2.0 * d * (M0 + C) * BH * N
+    k2_flops = 4.0 * d * (M0 + P * C) * BH * N
+    return {"assign_aggregate_kernel": (k1_bytes, k1_flops), "attention_kernel": (k2_bytes, k2_flops)}
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, P):
+    """The oracle as it stands, on the host cores: assignment, aggregation,
+    importance, top-P and the substituted-codebook output for the whole
+    workload (one run; OpenMP over the B*H heads)."""
+    import oracle
+    from adaptive_vector_quantized_amd import gen
+    data = gen.make(cfg)
+    o = oracle.Oracle.for_cfg(cfg)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    t0 = time.perf_counter()
+    o.forward(data["Q"], data["K"], data["V"], data["codebook"], P, cfg.block_q, cfg.scale)
+    dt = time.perf_counter() - t0
+    return {
+        "value": cfg.B * cfg.N / dt / 1e6,
+        "unit": "Mtokens/s",
+        "cores": min(threads, cfg.BH),
+        "kind": "oracle",
+        "sample": f"the whole workload ({cfg.B}x{cfg.H} heads x {cfg.N} tokens), one pass of the plain-C oracle "
+                  f"(assign, aggregate, importance, top-P, substituted-codebook output): {dt:.2f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--workload", default="grid128")
+    ap.add_argument("--P", type=int, default=None)
+    ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the forward pass shards over batch*heads with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from adaptive_vector_quantized_amd import _lib, gen
+
+    cfg = gen.CONFIGS[args.workload]
+    P = cfg.P if args.P is None else args.P
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def dev4(a):
+        return torch.from_numpy(a).to(tdt).reshape(cfg.B, cfg.H, cfg.N, cfg.d).contiguous().to(dev)
+
+    sets = []
+    for i in range(args.sets):
+        d = gen.make(cfg, seed=cfg.seed + 100 * i)
+        sets.append({
+            "Q": dev4(d["Q"]), "K": dev4(d["K"]), "V": dev4(d["V"]),
+            "cb": torch.from_numpy(d["codebook"]).to(tdt).contiguous().to(dev),
+            "vsum": torch.empty((cfg.B, cfg.H, cfg.Mt, cfg.d), dtype=torch.float32, device=dev),
+            "counts": torch.empty((cfg.B, cfg.H, cfg.Mt), dtype=torch.int32, device=dev),
+            "Y": torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.float32, device=dev),
+        })
+        del d
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: {args.sets} input sets resident, warmup {args.warmup}, steps {args.steps}",
+          file=sys.stderr, flush=True)
+
+    def step(s):
+        _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
+        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"])
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # timed region: per-kernel events on the launch stream inside every step
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        e = ev[i]
+        e[0].record(stream)
+        _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
+        e[1].record(stream)
+        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"])
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3  # seconds
+    k2 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    gpu_span = ev[0][0].elapsed_time(ev[-1][2]) * 1e-3
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms_per_step = wall / args.steps * 1e3
+    tokens = cfg.B * cfg.N
+    value = tokens / (wall / args.steps) / 1e6
+    alg = algorithmic(cfg, P)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    kernels = {}
+    for name, t in (("assign_aggregate_kernel", k1), ("attention_kernel", k2)):
+        b, f = alg[name]
+        avg = float(t.mean())
+        kernels[name] = {
+            "avg_us": avg * 1e6, "median_us": float(np.median(t)) * 1e6,
+            "algorithmic_bytes": b, "algorithmic_flops": f,
+            "GBps": b / avg / 1e9, "hbm_frac": b / avg / 1e9 / HBM_PEAK_GBS,
+            "TFLOPs": f / avg / 1e12, "mfma_frac": f / avg / 1e12 / mfma_peak,
+        }
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    kd = kernels[dom]
+    traffic = load_traffic(dom, cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Mtokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N}"
+                        + (f" ({cfg.grid}x{cfg.grid} token grid, 8x8-patch clusters)" if cfg.grid else "")
+                        + f" d={cfg.d} M0={cfg.M0} C={cfg.C} P={P} block_q={cfg.block_q}, {cfg.parents} parent occupancy",
+            "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kd["hbm_frac"], 4), "traffic": traffic,
+        },
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "gpu_span_ms_per_step": round(gpu_span / max(1, args.steps - 1) * 1e3, 5),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, P)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
