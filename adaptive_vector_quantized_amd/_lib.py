@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "avq.h")
 AVQ_F32 = 0
 AVQ_BF16 = 1
 STATUS = {0: "AVQ_OK", -1: "AVQ_ERR_NULL", -2: "AVQ_ERR_SHAPE", -3: "AVQ_ERR_DTYPE", -4: "AVQ_ERR_ALIGN",
-          -5: "AVQ_ERR_UNSUPPORTED", -6: "AVQ_ERR_HIP"}
+          -5: "AVQ_ERR_UNSUPPORTED", -6: "AVQ_ERR_HIP", -7: "AVQ_ERR_WORKSPACE"}
 
 
 class AvqError(RuntimeError):
@@ -38,8 +38,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.avq_assign_aggregate.argtypes = [P, P, P] + [i32] * 7 + [P, P, P, P]
     lib.avq_assign_aggregate.restype = i32
-    lib.avq_attention_fwd.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P]
+    lib.avq_attention_fwd.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P, ctypes.c_size_t, P]
     lib.avq_attention_fwd.restype = i32
+    lib.avq_attention_workspace_size.argtypes = [i32] * 6
+    lib.avq_attention_workspace_size.restype = ctypes.c_size_t
     lib.avq_status_string.argtypes = [i32]
     lib.avq_status_string.restype = ctypes.c_char_p
     lib.avq_version.argtypes = []
@@ -58,7 +60,7 @@ def lib() -> ctypes.CDLL:
 def declared_symbols(header: str = HEADER):
     """Names of the functions include/avq.h declares."""
     text = open(header).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(avq_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(avq_\w+)\s*\(", text, flags=re.M)))
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -111,11 +113,17 @@ def assign_aggregate(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C
     return vsum, counts, assign
 
 
+def workspace_size(B: int, H: int, d: int, M0: int, C: int, dtype: torch.dtype) -> int:
+    return int(_lib.avq_attention_workspace_size(B, H, d, M0, C, AVQ_BF16 if dtype == torch.bfloat16 else AVQ_F32))
+
+
 def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, counts: torch.Tensor, C: int, P: int,
                   block_q: int, scale: Optional[float] = None, *, want_topp: bool = False,
-                  want_importance: bool = False, Y: Optional[torch.Tensor] = None):
+                  want_importance: bool = False, Y: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
     """Kernel 2.  Q: [B, H, N, d]; codebook [H, Mt, d]; vsum/counts from assign_aggregate.
-    Returns (Y [B, H, N, d] float32, topp [B, H, T, P] int32 or None, importance [B, H, T, M0] or None)."""
+    Returns (Y [B, H, N, d] float32, topp [B, H, T, P] int32 or None, importance [B, H, T, M0] or None).
+    ``workspace`` (uint8 device tensor) is allocated here when not given."""
     B, H, N, d = _shape4(Q, "Q")
     Mt = codebook.shape[1]
     M0 = Mt // (1 + C)
@@ -127,12 +135,15 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
         Y = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     topp = torch.empty((B, H, T, P), dtype=torch.int32, device=dev) if want_topp else None
     imp = torch.empty((B, H, T, M0), dtype=torch.float32, device=dev) if want_importance else None
+    need = workspace_size(B, H, d, M0, C, Q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     for name, t in (("vsum", vsum), ("counts", counts)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     rc = _lib.avq_attention_fwd(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
                                 _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(imp),
-                                _stream(Q))
+                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(Q))
     if rc != 0:
         raise AvqError(rc, "avq_attention_fwd")
     return Y, topp, imp

@@ -68,23 +68,29 @@ int avq_assign_aggregate(const void* K, const void* V, const void* codebook, int
                                      assign, st));
 }
 
+size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C, int dtype) {
+  if (check_common(B, H, 0, d, M0, C, dtype) != AVQ_OK) return 0;
+  return avq::attention_workspace_bytes(dtype, d, M0, C, B * H);
+}
+
 int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H,
                       int N, int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y,
-                      int32_t* topp, float* importance, void* stream) {
+                      int32_t* topp, float* importance, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
   if (P < 0 || P > M0) return AVQ_ERR_SHAPE;
   if (block_q != 32 && block_q != 64 && block_q != 128) return AVQ_ERR_UNSUPPORTED;
-  if (!isfinite(scale)) return AVQ_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.0f)) return AVQ_ERR_SHAPE;
   const int64_t BH = (int64_t)B * H;
   if (BH == 0 || N == 0) return AVQ_OK;
-  if (!Q || !codebook || !vsum || !counts || !Y) return AVQ_ERR_NULL;
+  if (!Q || !codebook || !vsum || !counts || !Y || !workspace) return AVQ_ERR_NULL;
   if (!aligned16(Q) || !aligned16(codebook) || !aligned16(vsum) || !aligned16(counts) || !aligned16(Y) ||
-      (topp && !aligned16(topp)) || (importance && !aligned16(importance)))
+      !aligned16(workspace) || (topp && !aligned16(topp)) || (importance && !aligned16(importance)))
     return AVQ_ERR_ALIGN;
-  if (avq::attention_smem_bytes(dtype, d, M0, P, block_q) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
+  if (workspace_bytes < avq::attention_workspace_bytes(dtype, d, M0, C, (int)BH)) return AVQ_ERR_WORKSPACE;
+  if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
-                                        Y, topp, importance, (hipStream_t)stream));
+                                        Y, topp, importance, workspace, (hipStream_t)stream));
 }
 
 const char* avq_status_string(int status) {
@@ -96,6 +102,7 @@ const char* avq_status_string(int status) {
     case AVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case AVQ_ERR_UNSUPPORTED: return "unsupported size (d, M0, C, block_q or B*H)";
     case AVQ_ERR_HIP: return "HIP runtime error";
+    case AVQ_ERR_WORKSPACE: return "workspace smaller than avq_attention_workspace_size()";
     default: return "unknown status";
   }
 }

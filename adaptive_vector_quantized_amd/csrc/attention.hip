@@ -3,23 +3,40 @@
 // correction ("AVQ-Attention: Adaptive Vector-Quantized Attention",
 // Sec. 4.3 and Algorithm 2; Eq. 6-9; Sec. C and D).
 //
-// One workgroup per (query tile, batch*head); one wave per 32 queries.
-// Logits are computed transposed on MFMA (rows = codewords, columns =
-// queries): each lane owns one query and 16 codewords per 32-row block, so
-// the running max, the denominator and the rescaling are per-lane scalars,
-// the parent logit of Eq. 8 is a sum over registers of one lane, and the
-// weights feed the weighted-value MFMA as its B operand in place.
+// Two launches on the caller's stream:
 //
-// Value sums of the codewords in use are staged per chunk (up to 128
-// codewords) in LDS, transposed and, for bf16 inputs, converted to fp16
-// after scaling by a power of two chosen from the chunk's largest magnitude;
-// the accumulator carries the current scale and is re-expressed when the
-// next chunk's scale differs (an exact power-of-two factor folded into the
-// online-softmax rescale).
+//  1. attention_prep_kernel, once per (batch, head): the value sums are
+//     scaled by one power of two per (batch, head) (so that the largest
+//     magnitude lands in [2^14, 2^15) and fp16 keeps 11 significant bits of
+//     every value without overflow) and written to the workspace as fp16
+//     MFMA operand fragments, in exactly the order the attention kernel keeps
+//     them in LDS.  fp32 inputs keep fp32 values (scale 1).
 //
-// Children are packed S = 32 / W parents per 32-row block (W = slot width,
-// C <= W): the children of one selected parent occupy W consecutive
-// accumulator registers of one lane half, in child order.
+//  2. attention_kernel.  A workgroup owns a contiguous range of query tiles
+//     of one (batch, head); one wave handles 32 queries of a tile.  The
+//     parents' codeword and value fragments are copied into LDS once per
+//     workgroup; per tile, the selected parents' children are copied into LDS
+//     by asynchronous global-to-LDS loads (no registers held, one wait).
+//
+// Per tile.  Logits are computed transposed on MFMA (rows = codewords,
+// columns = queries): each lane owns one query and 16 codewords per 32-row
+// block, so the stabiliser, the denominator and the rescaling are per-lane
+// scalars, the parent logit of Eq. 8 is a sum over registers of one lane, and
+// the weights feed the weighted-value MFMA as its B operand in place.  The
+// importance of Eq. 7 is reduced over the 32 query lanes by a butterfly
+// reduce-scatter (permlane16 swap and DPP mirrors), then over the waves in
+// LDS; every wave ranks the parents itself, so the selection needs no second
+// barrier.
+//
+// The stabiliser follows Eq. 18 (max over non-empty codewords) but is only
+// raised when a new maximum exceeds it by more than 2^8: weights then stay in
+// [-2^8, 2^8], exactly representable ranges for the fp16 operand, and most
+// rescaling of the accumulators is skipped.  Empty codewords get logit -inf
+// (weight exactly 0), and a selected parent without keys gets a bounded
+// recovered weight, so no inf * 0 can arise (Sec. D).
+//
+// Children of a selected parent occupy W (8 or 16) consecutive accumulator
+// registers of one lane half, so S = 32 / W parents share a 32-row block.
 #include "avq_device.h"
 #include "avq_launch.h"
 
@@ -39,407 +56,586 @@ __device__ __forceinline__ typename T::pvfrag_t pack_at(const f32x16& v) {
   }
 }
 
-// Stage value sums and counts of ncols codewords into the transposed tile
-// sV[D][LDV] and sN[ncols]; rowof(c) is the codebook row of column c or -1.
-// Returns the scale sigma: staged values are vsum / sigma.
-template <class T, int D, int LDV, class RowFn>
-__device__ float stage_values(typename T::pv_t* sV, float* sN, float* sRed, const float* __restrict__ vs,
-                              const int* __restrict__ nb, int ncols, RowFn rowof, int tid, int nthreads,
-                              int lane, int wave, int nw) {
-  using pv_t = typename T::pv_t;
-  constexpr int C4 = D / 4;
-  const int items = ncols * C4;
-  float sig = 1.0f, inv = 1.0f;
-  if constexpr (T::kScaleValues) {
-    float mx = 0.0f;
-    for (int i = tid; i < items; i += nthreads) {
-      const int c = i / C4, q = (i % C4) * 4;
-      const int row = rowof(c);
-      if (row >= 0) {
-        const f32x4 v = *(const f32x4*)(vs + (int64_t)row * D + q);
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-      }
-    }
-    mx = wave_max(mx);
-    if (lane == 0) sRed[wave] = mx;
-    __syncthreads();
-    mx = 0.0f;
-    for (int w = 0; w < nw; ++w) mx = fmaxf(mx, sRed[w]);
-    if (mx > 0.0f) {
-      int e;
-      frexpf(mx, &e);  // mx < 2^e
-      sig = ldexpf(1.0f, e - 15);
-      inv = ldexpf(1.0f, 15 - e);
-    }
+template <class T, int KV>
+__device__ __forceinline__ typename T::pvfrag_t pv_operand(const f32x16& v, int k) {
+  if constexpr (KV == 2) {
+    return k == 0 ? pack_at<T, 0>(v) : pack_at<T, 8>(v);
+  } else {
+    return v[k];
   }
-  for (int i = tid; i < items; i += nthreads) {
-    const int c = i / C4, q = (i % C4) * 4;
-    const int row = rowof(c);
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (row >= 0) v = *(const f32x4*)(vs + (int64_t)row * D + q);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sV[(q + j) * LDV + c] = (pv_t)(v[j] * inv);
-  }
-  for (int c = tid; c < ncols; c += nthreads) {
-    const int row = rowof(c);
-    sN[c] = row >= 0 ? (float)nb[row] : 0.0f;
-  }
-  __syncthreads();
-  return sig;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// power of two sigma with max / sigma in [2^14, 2^15)
+__device__ __forceinline__ float value_scale(float mx) {
+  if (!(mx > 0.0f)) return 1.0f;
+  int e;
+  frexpf(mx, &e);
+  return ldexpf(1.0f, e - 15);
+}
+
+__device__ __forceinline__ float absmax4(f32x4 v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
+// parent index of value column c (columns are in accumulator-register order)
+__device__ __forceinline__ int parent_of_col(int c) {
+  const int q = c & 31;
+  return 32 * (c >> 5) + row_of(r_of_col(q), h_of_col(q));
+}
+
+// asynchronous copy of BYTES per lane from global memory into LDS at
+// lds_base + lane * BYTES (lds_base must be the same for the whole wave)
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* gptr, void* lds_base) {
+  static_assert(BYTES == 16 || BYTES == 4, "fragment size");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
 }  // namespace
 
+// ---- workspace layout ---------------------------------------------------------
+// [0, align256(4*BH))         scale sigma of every (batch, head)
+// then per (batch, head), align256(bytes) each:
+//   parent value fragments    (M0p/32 blocks) x [KV][2][D] fragments
+//   child value fragments     M0 parents x [W/E][D] fragments
+// A fragment is E consecutive operand elements (8 fp16, or 1 fp32).
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
+  const size_t pes = dtype == 0 ? 4 : 2;
+  const size_t M0p = (M0 + 31) & ~31;
+  const size_t W = C <= 8 ? 8 : 16;
+  const size_t per = align256((M0p * d + (size_t)M0 * W * d) * pes);
+  return align256((size_t)BH * 4) + (size_t)BH * per;
+}
+
 template <class T, int D, int W>
-__global__ __launch_bounds__(256) void attention_kernel(
-    const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb,
-    const float* __restrict__ vsum, const int* __restrict__ counts, int H, int N, int M0, int C, int P, int bq,
-    float sl2, float* __restrict__ Y, int* __restrict__ topp, float* __restrict__ importance) {
-  using in_t = typename T::in_t;
-  using frag_t = typename T::frag_t;
-  using pv_t = typename T::pv_t;
+__global__ __launch_bounds__(256) void attention_prep_kernel(const float* __restrict__ vsum, int M0, int C, int parts,
+                                                             unsigned char* __restrict__ ws, size_t sig_bytes,
+                                                             size_t per_bh) {
   using pvfrag_t = typename T::pvfrag_t;
   constexpr int E = T::E;
-  constexpr int KS = D / (2 * E);
-  constexpr int DB = D / 32;
-  constexpr int S = 32 / W;
-  constexpr int LDV = 128 + 16 / sizeof(pv_t);
-  constexpr int KV = 16 / E;  // weighted-value k-steps per 32-row block
+  constexpr int KV = 16 / E;
+  __shared__ float red[4];
+  const int bh = blockIdx.x / parts, part = blockIdx.x % parts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Mt = M0 * (1 + C);
+  const int M0p = (M0 + 31) & ~31;
+  const float* vs = vsum + (int64_t)bh * Mt * D;
+  float sig = 1.0f;
+  if constexpr (T::kScaleValues) {
+    float mx = 0.0f;
+    for (int i = tid; i < Mt * (D / 4); i += 256) mx = fmaxf(mx, absmax4(((const f32x4*)vs)[i]));
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    sig = value_scale(mx);
+  }
+  if (part == 0 && tid == 0) ((float*)ws)[bh] = sig;
+  const float inv = 1.0f / sig;
+  pvfrag_t* pf = (pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
+  const int nP = (M0p / 32) * KV * 2 * D;       // parent fragments
+  const int nC = M0 * (W / E) * D;              // child fragments
+  for (int f = part * 256 + tid; f < nP + nC; f += parts * 256) {
+    float x[E];
+    if (f < nP) {
+      const int d = f % D, t = f / D;
+      const int hh = t % 2, bk = t / 2, k = bk % KV, b = bk / KV;
+      const int c0 = b * 32 + 16 * ((k * E) >> 3) + 8 * hh + ((k * E) & 7);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int p = parent_of_col(c0 + j);
+        x[j] = p < M0 ? vs[(int64_t)p * D + d] * inv : 0.0f;
+      }
+    } else {
+      const int g2 = f - nP;
+      const int d = g2 % D, t = g2 / D;
+      const int g = t % (W / E), p = t / (W / E);
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const int c = g * E + j;
+        x[j] = c < C ? vs[(int64_t)(M0 + p * C + c) * D + d] * inv : 0.0f;
+      }
+    }
+    pf[f] = T::pack_pv(x);
+  }
+}
+
+template <class T, int D, int W>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
+    const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
+    const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
+    int bq, int tiles_per_wg, int wgs_per_bh, float sl2, float* __restrict__ Y, int* __restrict__ topp,
+    float* __restrict__ importance) {
+  using in_t = typename T::in_t;
+  using frag_t = typename T::frag_t;
+  using pvfrag_t = typename T::pvfrag_t;
+  constexpr int E = T::E;
+  constexpr int KS = D / (2 * E);   // logit k-steps over the head dimension
+  constexpr int DB = D / 32;        // 32-row blocks of the output dimension
+  constexpr int S = 32 / W;         // parents per 32-row child block
+  constexpr int KV = 16 / E;        // weighted-value k-steps per 32-row block
+  constexpr int CH = AttnTraits<D>::kChunkRows;
+  constexpr int NCB = CH / 32;
+  constexpr int FA = KS * 64;       // codeword fragments per 32-row block
+  constexpr int FV = KV * 2 * D;    // value fragments per 32-codeword block
+  constexpr int BA = (int)sizeof(frag_t);
+  constexpr int BV = (int)sizeof(pvfrag_t);
+  constexpr float kLazy = 8.0f;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int nthreads = blockDim.x;
   const int nw = nthreads >> 6;
   const int Mt = M0 * (1 + C);
   const int M0p = (M0 + 31) & ~31;
-  pv_t* sV = (pv_t*)smem;
-  float* sN = (float*)(sV + D * LDV);
-  float* sW = sN + 128;
-  float* sWt = sW + nw * M0p;
-  float* sRed = sWt + M0p;
-  int* sSel = (int*)(sRed + 8);
+  const int nblkP = M0p / 32;
+  const int Pp = P > 0 ? P : 1;
+  const bool parents_lds = M0p <= 64;  // parents' codewords in LDS (else read from L2)
+  frag_t* sPC = (frag_t*)smem;                                        // [nblkP*FA] if parents_lds
+  pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV]
+  frag_t* sCC = (frag_t*)(sPV + nblkP * FV);                          // [NCB*FA]
+  pvfrag_t* sCV = (pvfrag_t*)(sCC + NCB * FA);                        // [NCB*FV]
+  float* sNp = (float*)(sCV + NCB * FV);                              // [M0p]
+  float* sNc = sNp + M0p;                                             // [CH]
+  float* sW = sNc + CH;                                               // [nw][M0p]
+  float* sWv = sW + nw * M0p;                                         // [nw][M0p]
+  int* sSel = (int*)(sWv + nw * M0p);                                 // [nw][Pp]
+  int* sFlag = sSel + nw * Pp;                                        // [1]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.y, h = bh % H, tile = blockIdx.x;
-  const int ntiles = gridDim.x;
-  const int qi = tile * bq + wave * 32 + ql;
-  const bool qv = qi < N;
+  // Workgroups of one (batch, head) on one XCD when possible (consecutive
+  // workgroup ids go to the XCDs round robin): its data then lives in one L2.
+  int bh, g;
+  {
+    const int L = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int k = L >> 3;
+      bh = (k / wgs_per_bh) * 8 + (L & 7);
+      g = k % wgs_per_bh;
+    } else {
+      bh = L / wgs_per_bh;
+      g = L % wgs_per_bh;
+    }
+  }
+  const int h = bh % H;
+  const int ntiles = (N + bq - 1) / bq;
+  const int tile0 = g * tiles_per_wg;
+  const int tile1 = min(ntiles, tile0 + tiles_per_wg);
+  if (tile0 >= tile1) return;
   const in_t* cbh = cb + (int64_t)h * Mt * D;
-  const float* vs = vsum + (int64_t)bh * Mt * D;
   const int* nb = counts + (int64_t)bh * Mt;
+  const in_t* Qb = Q + (int64_t)bh * N * D;
+  float* Yb = Y + (int64_t)bh * N * D;
+  const float sig = ((const float*)ws)[bh];
+  const pvfrag_t* pvf = (const pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
+  const pvfrag_t* cvf = pvf + nblkP * FV;
+  const bool need_imp = (P > 0) || (importance != nullptr);
+  const int nPT = (M0 + 63) / 64;
 
+  // ---- once per workgroup: parents into LDS -----------------------------------
+  if (parents_lds) {
+    for (int u = wave; u < nblkP * KS; u += nw) {
+      const int b = u / KS, s = u % KS;
+      const int j = b * 32 + ql;
+      lds_dma<BA>(cbh + (int64_t)(j < M0 ? j : 0) * D + s * 2 * E + E * hh, sPC + u * 64);
+    }
+  }
+  for (int u = wave; u < nblkP * FV / 64; u += nw) lds_dma<BV>(pvf + u * 64 + lane, sPV + u * 64);
+  if (tid == 0) sFlag[0] = 1;
+  __syncthreads();
+  for (int c = tid; c < M0p; c += nthreads) {
+    const int j = parent_of_col(c);
+    const float n = j < M0 ? (float)nb[j] : 0.0f;
+    sNp[c] = n;
+    if (j < M0 && !(n > 0.0f)) sFlag[0] = 0;
+  }
   frag_t qf[KS];
   {
-    const in_t* qp = Q + ((int64_t)bh * N + (qv ? qi : N - 1)) * D + E * hh;
+    const int qi = tile0 * bq + wave * 32 + ql;
+    const in_t* qp = Qb + (int64_t)(qi < N ? qi : N - 1) * D + E * hh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = *(const frag_t*)(qp + s * 2 * E);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const bool all_parents = sFlag[0] != 0;
 
-  f32x16 xacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) xacc[db] = zero16();
-  float zp = 0.0f;        // denominator over this lane half's codewords
-  float m = -INFINITY;    // running max of the log2-scaled logits
-  float sig = 1.0f;       // xacc holds value sums divided by sig
-  const bool need_imp = (P > 0) || (importance != nullptr);
-  const int nPT = (M0 + 63) / 64;
-  f32x16 lg[2];
+  // ---- query tiles ------------------------------------------------------------
+  for (int tile = tile0; tile < tile1; ++tile) {
+    const int qi = tile * bq + wave * 32 + ql;
+    const bool qv = qi < N;
 
-  // ---- parents (Alg. 2 lines 2-7), in tiles of 64 --------------------------
-  for (int pt = 0; pt < nPT; ++pt) {
-    const int j0 = pt * 64;
-    const int nblk = min(2, (M0 - j0 + 31) / 32);
-    if (pt > 0) __syncthreads();
-    const float sg = stage_values<T, D, LDV>(
-        sV, sN, sRed, vs, nb, nblk * 32,
-        [&](int c) {
-          const int b = c >> 5, q = c & 31;
-          const int j = j0 + 32 * b + row_of(r_of_col(q), h_of_col(q));
-          return j < M0 ? j : -1;
-        },
-        tid, nthreads, lane, wave, nw);
+    f32x16 xacc[DB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      lg[b] = zero16();
-      if (b < nblk) {
-        const int j = j0 + 32 * b + ql;
-        const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], lg[b]);
-      }
-    }
-    float tm = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (b < nblk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          lg[b][r] *= sl2;
-          if (sN[b * 32 + col_of(r, hh)] > 0.0f) tm = fmaxf(tm, lg[b][r]);
-        }
-      }
-    }
-    tm = xhalf_max(tm);
-    const float mn = fmaxf(m, tm);
-    if (mn != -INFINITY) {
-      const float f = exp2f(m - mn);
-      zp *= f;
-      const float fx = f * (sig / sg);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) xacc[db] *= fx;
-      m = mn;
-      sig = sg;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (b < nblk) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float n = sN[b * 32 + col_of(r, hh)];
-            const float a = n > 0.0f ? exp2f(lg[b][r] - m) : 0.0f;
-            lg[b][r] = a;
-            zp = fmaf(a, n, zp);
-          }
-#pragma unroll
-          for (int k = 0; k < KV; ++k) {
-            pvfrag_t bf;
-            if constexpr (KV == 2) bf = k == 0 ? pack_at<T, 0>(lg[b]) : pack_at<T, 8>(lg[b]);
-            else bf = lg[b][k];
-            const int cofs = b * 32 + 16 * ((k * E) >> 3) + 8 * hh + ((k * E) & 7);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const pvfrag_t af = *(const pvfrag_t*)(sV + (db * 32 + ql) * LDV + cofs);
-              xacc[db] = T::mma_pv(af, bf, xacc[db]);
-            }
-          }
-        }
-      }
-    } else {
-      lg[0] = zero16();
-      lg[1] = zero16();
-    }
-  }
+    for (int db = 0; db < DB; ++db) xacc[db] = zero16();
+    float zp = 0.0f;       // denominator over this lane half's codewords
+    float m = -INFINITY;   // stabiliser of the scaled (log2-domain) logits
+    f32x16 lg[2];
 
-  // ---- importance (Eq. 7, Alg. 2 line 8) and top-P (line 9) ----------------
-  if (need_imp) {
-    const float zt = xhalf_sum(zp);
-    const float rz = qv ? 1.0f / zt : 0.0f;
+    // parents (Alg. 2 lines 2-7), 64 per pass
     for (int pt = 0; pt < nPT; ++pt) {
       const int j0 = pt * 64;
       const int nblk = min(2, (M0 - j0 + 31) / 32);
-      float t[32];
-      if (nPT == 1) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b) {
+        lg[b] = zero16();
+        if (b < nblk) {
+          const int bb = pt * 2 + b;
+          if (parents_lds) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            t[b * 16 + r] = b < nblk ? lg[b][r] * sN[b * 32 + col_of(r, hh)] * rz : 0.0f;
-      } else {
-        // second pass: logits again with the final max and denominator
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          f32x16 l2 = zero16();
-          if (b < nblk) {
-            const int j = j0 + 32 * b + ql;
+            for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
+          } else {
+            const int j = bb * 32 + ql;
             const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) l2 = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], l2);
+            for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], lg[b]);
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * b + row_of(r, hh);
-            const float n = (b < nblk && j < M0) ? (float)nb[j] : 0.0f;
-            t[b * 16 + r] = n > 0.0f ? exp2f(l2[r] * sl2 - m) * n * rz : 0.0f;
-          }
-        }
-      }
-      if (nblk == 2) {
-        rs_half32(t, lane);
-        const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
-        if (j < M0) sW[wave * M0p + j] = t[0];
-      } else {
-        rs_half16(t, lane);
-        const int j = j0 + row_of(ql & 15, hh);
-        if (ql < 16 && j < M0) sW[wave * M0p + j] = t[0];
-      }
-    }
-    __syncthreads();
-    for (int j = tid; j < M0; j += nthreads) {
-      float s = 0.0f;
-      for (int w = 0; w < nw; ++w) s += sW[w * M0p + j];
-      sWt[j] = s;
-      if (importance) importance[((int64_t)bh * ntiles + tile) * M0 + j] = s;
-    }
-    __syncthreads();
-    if (P > 0) {
-      if (wave == 0) {
-        int before = 0;
-        for (int jb = 0; jb < M0p; jb += 64) {
-          const int j = jb + lane;
-          bool sel = false;
-          if (j < M0) {
-            const float wj = sWt[j];
-            int rank = 0;
-            for (int jj = 0; jj < M0; ++jj) {
-              const float wo = sWt[jj];
-              rank += (wo > wj) || (wo == wj && jj < j);
-            }
-            sel = rank < P;
-          }
-          const uint64_t msk = __ballot(sel);
-          if (sel) {
-            const int pos = before + __popcll(msk & ((1ull << lane) - 1ull));
-            sSel[pos] = j;
-            if (topp) topp[((int64_t)bh * ntiles + tile) * P + pos] = j;
-          }
-          before += __popcll(msk);
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // ---- children of the selected parents (Alg. 2 lines 10-19) ---------------
-  if (P > 0) {
-    const float invC = 1.0f / (float)C;
-    const int nblkC = (P + S - 1) / S;
-    const int rr = r_of_row(ql), hr = h_of_row(ql);
-    const int s_row = 2 * (rr / W) + hr, c_row = rr % W;
-    for (int cb0 = 0; cb0 < nblkC; cb0 += 4) {
-      const int nbk = min(4, nblkC - cb0);
-      __syncthreads();
-      const float sg = stage_values<T, D, LDV>(
-          sV, sN, sRed, vs, nb, nbk * 32,
-          [&](int c) {
-            const int b = c >> 5, q = c & 31;
-            const int r = r_of_col(q), hc = h_of_col(q);
-            const int gs = (cb0 + b) * S + 2 * (r / W) + hc, cc = r % W;
-            return (gs < P && cc < C) ? M0 + sSel[gs] * C + cc : -1;
-          },
-          tid, nthreads, lane, wave, nw);
-      f32x16 cl[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        cl[b] = zero16();
-        if (b < nbk) {
-          const int gs = (cb0 + b) * S + s_row;
-          const int row = (gs < P && c_row < C) ? M0 + sSel[gs] * C + c_row : 0;
-          const in_t* ap = cbh + (int64_t)row * D + E * hh;
-#pragma unroll
-          for (int s = 0; s < KS; ++s) cl[b] = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], cl[b]);
         }
       }
       float tm = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < nbk) {
+      for (int b = 0; b < 2; ++b) {
+        if (b < nblk) {
+          if (!all_parents || j0 + 32 * (b + 1) > M0) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            cl[b][r] *= sl2;
-            if (sN[b * 32 + col_of(r, hh)] > 0.0f) tm = fmaxf(tm, cl[b][r]);
+            for (int r = 0; r < 16; ++r)
+              if (!(sNp[j0 + b * 32 + col_of(r, hh)] > 0.0f)) lg[b][r] = -INFINITY;
           }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tm = fmaxf(tm, lg[b][r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lg[b][r] = -INFINITY;
         }
       }
-      tm = xhalf_max(tm);
-      const float mn = fmaxf(m, tm);
-      const float f = exp2f(m - mn);
-      zp *= f;
-      const float fx = f * (sig / sg);
+      tm = xhalf_max(tm) * sl2;
+      if (tm > m + kLazy || m == -INFINITY) {
+        const float mn = fmaxf(m, tm);
+        if (mn != -INFINITY) {
+          const float f = fast_exp2(m - mn);
+          zp *= f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) xacc[db] *= fx;
-      m = mn;
-      sig = sg;
+          for (int db = 0; db < DB; ++db) xacc[db] *= f;
+          m = mn;
+        }
+      }
+      if (m != -INFINITY) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < nbk) {
+        for (int b = 0; b < 2; ++b) {
+          if (b < nblk) {
 #pragma unroll
-          for (int g = 0; g < 16 / W; ++g) {
-            float sp = 0.0f;
+            for (int r = 0; r < 16; ++r) {
+              const float a = fast_exp2(fmaf(lg[b][r], sl2, -m));
+              lg[b][r] = a;
+              zp = fmaf(a, sNp[j0 + b * 32 + col_of(r, hh)], zp);
+            }
+            const int bb = pt * 2 + b;
 #pragma unroll
-            for (int c = 0; c < W; ++c)
-              if (c < C) sp += cl[b][g * W + c];
-            const float ap = exp2f(sp * invC - m);
+            for (int k = 0; k < KV; ++k) {
+              const pvfrag_t bf = pv_operand<T, KV>(lg[b], k);
 #pragma unroll
-            for (int c = 0; c < W; ++c) {
-              const float n = sN[b * 32 + col_of(g * W + c, hh)];
-              const float da = (c < C && n > 0.0f) ? exp2f(cl[b][g * W + c] - m) - ap : 0.0f;
-              cl[b][g * W + c] = da;
-              zp = fmaf(da, n, zp);
+              for (int db = 0; db < DB; ++db)
+                xacc[db] = T::mma_pv(sPV[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
+            }
+          } else {
+            lg[b] = zero16();
+          }
+        }
+      } else {
+        lg[0] = zero16();
+        lg[1] = zero16();
+      }
+    }
+
+    // importance (Eq. 7, Alg. 2 line 8) and top-P (line 9)
+    if (need_imp) {
+      const float rz = qv ? 1.0f / xhalf_sum(zp) : 0.0f;
+      for (int pt = 0; pt < nPT; ++pt) {
+        const int j0 = pt * 64;
+        const int nblk = min(2, (M0 - j0 + 31) / 32);
+        float t[32];
+        if (nPT == 1) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * sNp[b * 32 + col_of(r, hh)] * rz;
+        } else {
+          // second pass with the final stabiliser and denominator (exact Z of Eq. 7)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            f32x16 l2 = zero16();
+            if (b < nblk) {
+              const int j = j0 + 32 * b + ql;
+              const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
+#pragma unroll
+              for (int s = 0; s < KS; ++s) l2 = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], l2);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float n = b < nblk ? sNp[j0 + b * 32 + col_of(r, hh)] : 0.0f;
+              t[b * 16 + r] = n > 0.0f ? fast_exp2(fmaf(l2[r], sl2, -m)) * n * rz : 0.0f;
             }
           }
+        }
+        if (nblk == 2) {
+          rs_half32(t, lane);
+          const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
+          if (j < M0) sW[wave * M0p + j] = t[0];
+        } else {
+          rs_half16(t, lane);
+          const int j = j0 + row_of(ql & 15, hh);
+          if (ql < 16 && j < M0) sW[wave * M0p + j] = t[0];
+        }
+      }
+      __syncthreads();
+      // every wave forms the totals and its own copy of the selection
+      float* wv = sWv + wave * M0p;
+      for (int j = lane; j < M0p; j += 64) {
+        float s = -INFINITY;
+        if (j < M0) {
+          s = 0.0f;
+          for (int w = 0; w < nw; ++w) s += sW[w * M0p + j];
+          if (importance && wave == 0) importance[((int64_t)bh * ntiles + tile) * M0 + j] = s;
+        }
+        wv[j] = s;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (P > 0) {
+        int before = 0;
+        for (int jb = 0; jb < M0p; jb += 64) {
+          const int j = jb + lane;
+          const float wj = j < M0p ? wv[j] : -INFINITY;
+          int rank = 0;
+#pragma unroll 4
+          for (int q4 = 0; q4 < M0p; q4 += 4) {
+            const f32x4 w4 = *(const f32x4*)(wv + q4);
 #pragma unroll
-          for (int k = 0; k < KV; ++k) {
-            pvfrag_t bf;
-            if constexpr (KV == 2) bf = k == 0 ? pack_at<T, 0>(cl[b]) : pack_at<T, 8>(cl[b]);
-            else bf = cl[b][k];
-            const int cofs = b * 32 + 16 * ((k * E) >> 3) + 8 * hh + ((k * E) & 7);
+            for (int u = 0; u < 4; ++u) rank += (w4[u] > wj) || (w4[u] == wj && q4 + u < j);
+          }
+          const bool sel = j < M0 && rank < P;
+          const uint64_t msk = __ballot(sel);
+          if (sel) {
+            const int pos = before + __popcll(msk & ((1ull << lane) - 1ull));
+            sSel[wave * Pp + pos] = j;
+            if (topp && wave == 0) topp[((int64_t)bh * ntiles + tile) * P + pos] = j;
+          }
+          before += __popcll(msk);
+        }
+        __builtin_amdgcn_wave_barrier();
+      } else {
+        __syncthreads();  // partials are rewritten by the next tile; no staging barrier follows
+      }
+    }
+
+    frag_t qn[KS];
+    auto prefetch_next = [&]() {
+      const int qn_i = (tile + 1) * bq + wave * 32 + ql;
+      const in_t* qp = Qb + (int64_t)(qn_i < N ? qn_i : N - 1) * D + E * hh;
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const pvfrag_t af = *(const pvfrag_t*)(sV + (db * 32 + ql) * LDV + cofs);
-              xacc[db] = T::mma_pv(af, bf, xacc[db]);
+      for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
+    };
+    if (P == 0) prefetch_next();
+
+    // children of the selected parents (Alg. 2 lines 10-19), CH rows per chunk
+    if (P > 0) {
+      const int* sel = sSel + wave * Pp;
+      const float invC = 1.0f / (float)C;
+      for (int cs = 0; cs < P; cs += NCB * S) {
+        const int nbk = min(NCB, (P - cs + S - 1) / S);
+        if (cs > 0) __syncthreads();  // readers of the previous chunk are done
+        // codeword fragments: one DMA per (block, k-step); lane = (row, half)
+        {
+          const int r = r_of_row(ql), hr = h_of_row(ql);
+          const int s_row = 2 * (r / W) + hr, c_row = r % W;
+          for (int u = wave; u < nbk * KS; u += nw) {
+            const int b = u / KS, s = u % KS;
+            const int gs = cs + b * S + s_row;
+            const int row = (gs < P && c_row < C) ? M0 + sel[gs] * C + c_row : M0 + sel[0] * C;
+            lds_dma<BA>(cbh + (int64_t)row * D + s * 2 * E + E * hh, sCC + u * 64);
+          }
+        }
+        // value fragments: one DMA per (block, k-step, half, 64 dims); lane = dim
+        for (int u = wave; u < nbk * KV * 2 * (D / 64); u += nw) {
+          const int dc = u % (D / 64), t = u / (D / 64);
+          const int h2 = t % 2, bk = t / 2, k = bk % KV, b = bk / KV;
+          const int r = k * E;
+          const int gs = cs + b * S + 2 * (r / W) + h2, gg = (r % W) / E;
+          const int p = gs < P ? sel[gs] : sel[0];
+          lds_dma<BV>(cvf + ((int64_t)p * (W / E) + gg) * D + dc * 64 + lane, sCV + ((b * KV + k) * 2 + h2) * D + dc * 64);
+        }
+        for (int c = tid; c < nbk * 32; c += nthreads) {
+          const int b = c >> 5, qq = c & 31;
+          const int r = r_of_col(qq), hc = h_of_col(qq);
+          const int gs = cs + b * S + 2 * (r / W) + hc, cc = r % W;
+          sNc[c] = (gs < P && cc < C) ? (float)nb[M0 + sel[gs] * C + cc] : 0.0f;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (cs == 0) prefetch_next();
+
+        // logits of the whole chunk, masked (empty children -> -inf), one max
+        f32x16 cl[NCB];
+#pragma unroll
+        for (int b = 0; b < NCB; ++b) {
+          cl[b] = zero16();
+          if (b < nbk) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) cl[b] = T::mma_in(sCC[(b * KS + s) * 64 + lane], qf[s], cl[b]);
+          }
+        }
+        float tm = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NCB; ++b)
+          if (b < nbk) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, sNc[b * 32 + col_of(r, hh)] > 0.0f ? cl[b][r] : -INFINITY);
+          }
+        tm = xhalf_max(tm) * sl2;
+        if (tm > m + kLazy) {
+          const float f = fast_exp2(m - tm);
+          zp *= f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) xacc[db] *= f;
+          m = tm;
+        }
+#pragma unroll
+        for (int b = 0; b < NCB; ++b) {
+          if (b < nbk) {
+#pragma unroll
+            for (int g2 = 0; g2 < 16 / W; ++g2) {
+              float sp = 0.0f;
+#pragma unroll
+              for (int c = 0; c < W; ++c)
+                if (c < C) sp += cl[b][g2 * W + c];
+              // a slot beyond P contributes nothing; an empty selected parent
+              // gets a bounded weight (its children carry zero values/counts)
+              const bool slot_ok = cs + b * S + 2 * g2 + hh < P;
+              const float ap = slot_ok ? fast_exp2(fminf(fmaf(sp * invC, sl2, -m), kLazy + 1.0f)) : 0.0f;
+#pragma unroll
+              for (int c = 0; c < W; ++c) {
+                const float n = sNc[b * 32 + col_of(g2 * W + c, hh)];
+                const float e = n > 0.0f ? fast_exp2(fmaf(cl[b][g2 * W + c], sl2, -m)) : 0.0f;
+                const float da = (c < C) ? e - ap : 0.0f;
+                cl[b][g2 * W + c] = da;
+                zp = fmaf(da, n, zp);
+              }
+            }
+#pragma unroll
+            for (int k = 0; k < KV; ++k) {
+              const pvfrag_t bf = pv_operand<T, KV>(cl[b], k);
+#pragma unroll
+              for (int db = 0; db < DB; ++db)
+                xacc[db] = T::mma_pv(sCV[((b * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
             }
           }
         }
       }
     }
-  }
 
-  // ---- Y = x / z (Alg. 2 line 20) -------------------------------------------
-  const float zt = xhalf_sum(zp);
-  if (qv) {
-    const float f = sig / zt;
-    float* yp = Y + ((int64_t)bh * N + qi) * D + 4 * hh;
+    // Y = x / z (Alg. 2 line 20)
+    const float zt = xhalf_sum(zp);
+    if (qv) {
+      const float f = sig / zt;
+      float* yp = Yb + (int64_t)qi * D + 4 * hh;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 o = {xacc[db][4 * i] * f, xacc[db][4 * i + 1] * f, xacc[db][4 * i + 2] * f, xacc[db][4 * i + 3] * f};
-        *(f32x4*)(yp + db * 32 + 8 * i) = o;
-      }
+        for (int i = 0; i < 4; ++i) {
+          f32x4 o = {xacc[db][4 * i] * f, xacc[db][4 * i + 1] * f, xacc[db][4 * i + 2] * f, xacc[db][4 * i + 3] * f};
+          *(f32x4*)(yp + db * 32 + 8 * i) = o;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = qn[s];
   }
 }
 
-size_t attention_smem_bytes(int dtype, int d, int M0, int P, int block_q) {
-  const size_t pes = dtype == 0 ? 4 : 2;
-  const size_t ldv = 128 + 16 / pes;
+size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q) {
+  const size_t es = dtype == 0 ? 4 : 2;   // input and value operand element (same width)
   const size_t M0p = (M0 + 31) & ~31;
   const size_t nw = block_q / 32;
-  return d * ldv * pes + 128 * 4 + nw * M0p * 4 + M0p * 4 + 8 * 4 + (size_t)(P > 0 ? P : 1) * 4;
+  const size_t CH = d == 64 ? AttnTraits<64>::kChunkRows : AttnTraits<128>::kChunkRows;
+  (void)C;
+  size_t b = (M0p <= 64 ? M0p * d * es : 0);  // parents' codeword fragments
+  b += M0p * d * es;                          // parents' value fragments
+  b += 2 * CH * d * es;                       // chunk codeword and value fragments
+  b += (M0p + CH) * 4;                        // counts
+  b += 2 * nw * M0p * 4;                      // importance partials and totals
+  b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
+  return b;
+}
+
+// Query tiles per workgroup: aim for about two resident workgroups per CU.
+int attention_tiles_per_wg(int BH, int N, int bq) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  const int T = (N + bq - 1) / bq;
+  const int target = 2 * cus;
+  int per_bh = (target + BH - 1) / (BH > 0 ? BH : 1);
+  if (per_bh > T) per_bh = T;
+  if (per_bh < 1) per_bh = 1;
+  return (T + per_bh - 1) / per_bh;
 }
 
 template <class T, int D, int W>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                hipStream_t st) {
-  const size_t smem = attention_smem_bytes(std::is_same<T, TF32>::value ? 0 : 1, D, M0, P, bq);
+                                void* ws, hipStream_t st) {
+  const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
+  const size_t sig_bytes = align256((size_t)BH * 4);
+  const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
+  {
+    const int parts = 4;
+    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(256), 0, st, vsum, M0, C, parts,
+                       (unsigned char*)ws, sig_bytes, per_bh);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t smem = attention_smem_bytes(dtype, D, M0, C, P, bq);
   auto kern = attention_kernel<T, D, W>;
   hipError_t e = raise_lds_limit((const void*)kern, smem);
   if (e != hipSuccess) return e;
-  dim3 grid((N + bq - 1) / bq, BH);
+  const int tpw = attention_tiles_per_wg(BH, N, bq);
+  const int T_ = (N + bq - 1) / bq;
+  const int per = (T_ + tpw - 1) / tpw;
   const float sl2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(kern, grid, dim3(2 * bq), smem, st, (const typename T::in_t*)Q, (const typename T::in_t*)cb,
-                     vsum, counts, H, N, M0, C, P, bq, sl2, Y, topp, importance);
+  hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
+                     (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N, M0, C,
+                     P, bq, tpw, per, sl2, Y, topp, importance);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                hipStream_t st) {
-  if (C <= 4) return launch_attn_t<T, D, 4>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
-  if (C <= 8) return launch_attn_t<T, D, 8>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
-  return launch_attn_t<T, D, 16>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
+                                void* ws, hipStream_t st) {
+  if (C <= 8) return launch_attn_t<T, D, 8>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  return launch_attn_t<T, D, 16>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, hipStream_t st) {
+                            float* importance, void* ws, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
-    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
+    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
   }
-  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
-  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, st);
+  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
 }
 
 }  // namespace avq

@@ -145,6 +145,8 @@ def main():
             "vsum": torch.empty((cfg.B, cfg.H, cfg.Mt, cfg.d), dtype=torch.float32, device=dev),
             "counts": torch.empty((cfg.B, cfg.H, cfg.Mt), dtype=torch.int32, device=dev),
             "Y": torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.float32, device=dev),
+            "ws": torch.empty(_lib.workspace_size(cfg.B, cfg.H, cfg.d, cfg.M0, cfg.C, tdt), dtype=torch.uint8,
+                              device=dev),
         })
         del d
     torch.cuda.synchronize()
@@ -153,7 +155,8 @@ def main():
 
     def step(s):
         _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
-        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"])
+        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"],
+                           workspace=s["ws"])
 
     for i in range(args.warmup):
         step(sets[i % len(sets)])
@@ -170,7 +173,8 @@ def main():
         e[0].record(stream)
         _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
         e[1].record(stream)
-        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"])
+        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"],
+                           workspace=s["ws"])
         e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -17,8 +17,8 @@
  * --------------------------------
  * Pointers are device pointers (memory from hipMalloc or any allocator that
  * returns device memory), owned by the caller.  The library allocates no
- * device or host memory, keeps no state between calls and is safe to call
- * from several host threads.  Calls are asynchronous on `stream` (a
+ * device or host memory, keeps no results between calls and is safe to call
+ * from several host threads (calls sharing a workspace must not overlap).  Calls are asynchronous on `stream` (a
  * hipStream_t; NULL is the default stream).
  *
  * Shapes (all row-major and contiguous):
@@ -46,6 +46,7 @@
 #ifndef AVQ_H
 #define AVQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -59,6 +60,7 @@ extern "C" {
 #define AVQ_ERR_ALIGN (-4)       /* a pointer is not 16-byte aligned */
 #define AVQ_ERR_UNSUPPORTED (-5) /* valid but unsupported (d, M0, C, block_q) */
 #define AVQ_ERR_HIP (-6)         /* the HIP runtime reported an error */
+#define AVQ_ERR_WORKSPACE (-7)   /* workspace missing or too small */
 
 #define AVQ_F32 0
 #define AVQ_BF16 1
@@ -91,6 +93,15 @@ int avq_assign_aggregate(const void* K, const void* V, const void* codebook,
                          void* stream);
 
 /*
+ * Bytes of device workspace avq_attention_fwd needs for these sizes (0 if the
+ * sizes are invalid).  The workspace holds the value sums of every codeword
+ * converted to the operand format of the weighted-value products; it is
+ * written and read by one call and carries nothing between calls.
+ */
+size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C,
+                                    int dtype);
+
+/*
  * AVQ attention forward (Sec. 4.3, Algorithm 2; Eq. 6-9, Sec. C and D).
  *
  * Queries are processed in tiles of block_q consecutive tokens (the last tile
@@ -100,11 +111,13 @@ int avq_assign_aggregate(const void* K, const void* V, const void* codebook,
  *   X_i = sum_j A_ij Vsum_j, Z_i = sum_j A_ij n_j (Eq. 6);
  *   w_j = sum_{i in tile} A_ij n_j / Z_i (Eq. 7);
  *   the P parents of largest w (ties to the lower index) are refined: for
- *   their children c, s_ic = scale * Q_i . C_c, the running max is merged,
+ *   their children c, s_ic = scale * Q_i . C_c,
  *   s_ip = mean over the C children of s_ic (Eq. 8, needs Eq. 5),
  *   dA_ic = exp(s_ic - m_i) - exp(s_ip - m_i), zero where n_c = 0 (Eq. 9,
  *   Sec. D), X_i += sum_c dA_ic Vsum_c, Z_i += sum_c dA_ic n_c;
  *   Y_i = X_i / Z_i.
+ * The stabiliser m_i is raised (and the accumulators rescaled) only when a
+ * larger logit exceeds it by a factor 2^8; the result does not depend on it.
  * When M0 > 64 the parents are processed in tiles of 64 and the exact
  * denominator Z_i is completed in a first pass before the importances are
  * formed in a second pass.
@@ -115,22 +128,25 @@ int avq_assign_aggregate(const void* K, const void* V, const void* codebook,
  *   counts     in  [BH, Mt]    int32  (from avq_assign_aggregate)
  *   P          0 <= P <= M0 (P = 0: plain VQ attention over the parents)
  *   block_q    query tile: 32, 64 or 128 (one wave of 64 lanes per 32 queries)
- *   scale      logit scale (1/sqrt(d) in the usual convention, Sec. 3.1)
+ *   scale      logit scale, > 0 (1/sqrt(d) in the usual convention, Sec. 3.1)
  *   Y          out [BH, N, d] float
  *   topp       out [BH, ceil(N/block_q), P] int32, the selected parents of
  *              each tile in ascending order, or NULL to skip
  *   importance out [BH, ceil(N/block_q), M0] float, w_j per tile, or NULL
+ *   workspace  device memory of at least avq_attention_workspace_size()
+ *              bytes (AVQ_ERR_WORKSPACE otherwise); overwritten by the call
  *
  * Precision (bf16 inputs): logits use bf16 inputs with float accumulation;
- * the weighted value sums use fp16 operands (weights in [-1, 1], value sums
- * scaled by a power of two per codeword chunk) with float accumulation;
+ * the weighted value sums use fp16 operands (weights in [-2^8, 2^8], value
+ * sums scaled by one power of two per (batch, head)) with float accumulation;
  * softmax bookkeeping, denominators and importances are float.  fp32 inputs
  * use float throughout.
  */
 int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum,
                       const int32_t* counts, int B, int H, int N, int d, int M0,
                       int C, int dtype, int P, int block_q, float scale,
-                      float* Y, int32_t* topp, float* importance, void* stream);
+                      float* Y, int32_t* topp, float* importance,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* avq_status_string(int status);

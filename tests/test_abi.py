@@ -21,7 +21,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
-    assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_status_string", "avq_version"}
+    assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_attention_workspace_size",
+                          "avq_status_string", "avq_version"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -31,7 +32,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_strings(L):
     assert L.avq_version() == 100
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         assert L.avq_status_string(code)
 
 
@@ -53,10 +54,11 @@ def _assign(L, **kw):
 def _attn(L, **kw):
     _, p = _buf()
     a = dict(Q=p, cb=p, vsum=p, counts=p, B=1, H=1, N=8, d=64, M0=4, C=2, dtype=1, P=2, bq=64, scale=0.125,
-             Y=p, topp=None, imp=None)
+             Y=p, topp=None, imp=None, ws=p, wsb=1 << 30)
     a.update(kw)
     return L.avq_attention_fwd(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"], a["M0"],
-                               a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"], a["imp"], None)
+                               a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"], a["imp"],
+                               a["ws"], a["wsb"], None)
 
 
 def test_assign_validation(L):
@@ -96,6 +98,13 @@ def test_attention_validation(L):
     assert _attn(L, counts=None) == -1
     assert _attn(L, Y=mis) == -4
     assert _attn(L, topp=mis) == -4
+    assert _attn(L, scale=0.0) == -2
+    assert _attn(L, ws=None) == -1
+    assert _attn(L, ws=mis) == -4
+    need = L.avq_attention_workspace_size(1, 1, 64, 4, 2, 1)
+    assert need > 0
+    assert _attn(L, wsb=need - 1) == -7
+    assert L.avq_attention_workspace_size(1, 1, 96, 4, 2, 1) == 0   # invalid sizes
     assert _attn(L, N=0) == 0         # no queries: nothing to do
     assert _attn(L, B=0, Q=None) == 0
 
