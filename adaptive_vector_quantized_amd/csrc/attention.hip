@@ -96,22 +96,62 @@ __device__ __forceinline__ void lds_dma(const void* gptr, void* lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
+// Top-P of Alg. 2 over the importances one wave holds (parent j = 64 g + lane
+// in u[g]; non-negative floats as bit patterns, so integer order is value
+// order).  A radix search on the bits finds the P-th largest value thr; the
+// chosen set is everything above thr plus the lowest-index parents equal to
+// it (the tie rule of the oracle), written ascending to out[0..P).
+template <int NG>
+__device__ __forceinline__ void select_top(const uint32_t (&u)[NG], int M0, int P, int lane, int* out, int* gout) {
+  uint32_t thr = 0;
+#pragma unroll 2
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) cnt += __popcll(__ballot(u[g] >= cand));
+    thr = cnt >= P ? cand : thr;
+  }
+  int above = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) above += __popcll(__ballot(u[g] > thr));
+  const uint64_t below_me = (1ull << lane) - 1ull;
+  int eq_before = 0, before = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bool valid = g * 64 + lane < M0;
+    const bool eq = valid && u[g] == thr;
+    const uint64_t meq = __ballot(eq);
+    const bool sel = (valid && u[g] > thr) || (eq && eq_before + __popcll(meq & below_me) < P - above);
+    const uint64_t msk = __ballot(sel);
+    if (sel) {
+      const int pos = before + __popcll(msk & below_me);
+      out[pos] = g * 64 + lane;
+      if (gout) gout[pos] = g * 64 + lane;
+    }
+    before += __popcll(msk);
+    eq_before += __popcll(meq);
+  }
+}
+
 }  // namespace
 
 // ---- workspace layout ---------------------------------------------------------
 // [0, align256(4*BH))         scale sigma of every (batch, head)
+// then kZeroBytes of zeros    (source of the codeword rows of padding children)
 // then per (batch, head), align256(bytes) each:
 //   parent value fragments    (M0p/32 blocks) x [KV][2][D] fragments
 //   child value fragments     M0 parents x [W/E][D] fragments
 // A fragment is E consecutive operand elements (8 fp16, or 1 fp32).
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr int kZeroBytes = 256;
 
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   const size_t pes = dtype == 0 ? 4 : 2;
   const size_t M0p = (M0 + 31) & ~31;
   const size_t W = C <= 8 ? 8 : 16;
   const size_t per = align256((M0p * d + (size_t)M0 * W * d) * pes);
-  return align256((size_t)BH * 4) + (size_t)BH * per;
+  return align256((size_t)BH * 4) + kZeroBytes + (size_t)BH * per;
 }
 
 template <class T, int D, int W>
@@ -138,6 +178,7 @@ __global__ __launch_bounds__(256) void attention_prep_kernel(const float* __rest
     sig = value_scale(mx);
   }
   if (part == 0 && tid == 0) ((float*)ws)[bh] = sig;
+  if (blockIdx.x == 0 && tid < kZeroBytes / 4) ((float*)(ws + sig_bytes - kZeroBytes))[tid] = 0.0f;
   const float inv = 1.0f / sig;
   pvfrag_t* pf = (pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
   const int nP = (M0p / 32) * KV * 2 * D;       // parent fragments
@@ -201,11 +242,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV]
   frag_t* sCC = (frag_t*)(sPV + nblkP * FV);                          // [NCB*FA]
   pvfrag_t* sCV = (pvfrag_t*)(sCC + NCB * FA);                        // [NCB*FV]
-  float* sNp = (float*)(sCV + NCB * FV);                              // [M0p]
+  float* sNp = (float*)(sCV + NCB * FV);                              // [M0p] counts
   float* sNc = sNp + M0p;                                             // [CH]
-  float* sW = sNc + CH;                                               // [nw][M0p]
-  float* sWv = sW + nw * M0p;                                         // [nw][M0p]
-  int* sSel = (int*)(sWv + nw * M0p);                                 // [nw][Pp]
+  float* sBp = sNc + CH;                                              // [M0p] 0 or -inf (empty)
+  float* sBc = sBp + M0p;                                             // [CH]
+  float* sW = sBc + CH;                                               // [nw][M0p]
+  int* sSel = (int*)(sW + nw * M0p);                                  // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [1]
 
   const int tid = threadIdx.x;
@@ -236,6 +278,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* Yb = Y + (int64_t)bh * N * D;
   const float sig = ((const float*)ws)[bh];
   const pvfrag_t* pvf = (const pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
+  const unsigned char* zeros = ws + sig_bytes - kZeroBytes;  // codeword rows past C
   const pvfrag_t* cvf = pvf + nblkP * FV;
   const bool need_imp = (P > 0) || (importance != nullptr);
   const int nPT = (M0 + 63) / 64;
@@ -255,6 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int j = parent_of_col(c);
     const float n = j < M0 ? (float)nb[j] : 0.0f;
     sNp[c] = n;
+    sBp[c] = n > 0.0f ? 0.0f : -INFINITY;
     if (j < M0 && !(n > 0.0f)) sFlag[0] = 0;
   }
   frag_t qf[KS];
@@ -305,9 +349,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int b = 0; b < 2; ++b) {
         if (b < nblk) {
           if (!all_parents || j0 + 32 * (b + 1) > M0) {
+            const f32x4* bp = (const f32x4*)(sBp + j0 + b * 32 + 8 * hh);
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (!(sNp[j0 + b * 32 + col_of(r, hh)] > 0.0f)) lg[b][r] = -INFINITY;
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) lg[b][q * 4 + u] += b4[u];
+            }
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) tm = fmaxf(tm, lg[b][r]);
@@ -331,11 +379,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           if (b < nblk) {
+            const f32x4* np4 = (const f32x4*)(sNp + j0 + b * 32 + 8 * hh);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float a = fast_exp2(fmaf(lg[b][r], sl2, -m));
-              lg[b][r] = a;
-              zp = fmaf(a, sNp[j0 + b * 32 + col_of(r, hh)], zp);
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 n4 = np4[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const float a = fast_exp2(fmaf(lg[b][q * 4 + u], sl2, -m));
+                lg[b][q * 4 + u] = a;
+                zp = fmaf(a, n4[u], zp);
+              }
             }
             const int bb = pt * 2 + b;
 #pragma unroll
@@ -364,9 +417,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         float t[32];
         if (nPT == 1) {
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < 2; ++b) {
+            const f32x4* np4 = (const f32x4*)(sNp + b * 32 + 8 * hh);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * sNp[b * 32 + col_of(r, hh)] * rz;
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 n4 = np4[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) t[b * 16 + q * 4 + u] = lg[b][q * 4 + u] * (n4[u] * rz);
+            }
+          }
         } else {
           // second pass with the final stabiliser and denominator (exact Z of Eq. 7)
 #pragma unroll
@@ -397,37 +456,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
       __syncthreads();
       // every wave forms the totals and its own copy of the selection
-      float* wv = sWv + wave * M0p;
-      for (int j = lane; j < M0p; j += 64) {
-        float s = -INFINITY;
-        if (j < M0) {
-          s = 0.0f;
-          for (int w = 0; w < nw; ++w) s += sW[w * M0p + j];
+      constexpr int MAXG = 4;  // up to 256 parents, one per lane per group
+      uint32_t u[MAXG];
+#pragma unroll
+      for (int g = 0; g < MAXG; ++g) {
+        const int j = g * 64 + lane;
+        float s = 0.0f;
+        if (g * 64 < M0 && j < M0) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (w < nw) s += sW[w * M0p + j];
           if (importance && wave == 0) importance[((int64_t)bh * ntiles + tile) * M0 + j] = s;
         }
-        wv[j] = s;
+        u[g] = __float_as_uint(s);  // 0 past M0: never above a threshold search candidate
       }
-      __builtin_amdgcn_wave_barrier();
       if (P > 0) {
-        int before = 0;
-        for (int jb = 0; jb < M0p; jb += 64) {
-          const int j = jb + lane;
-          const float wj = j < M0p ? wv[j] : -INFINITY;
-          int rank = 0;
-#pragma unroll 4
-          for (int q4 = 0; q4 < M0p; q4 += 4) {
-            const f32x4 w4 = *(const f32x4*)(wv + q4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) rank += (w4[u] > wj) || (w4[u] == wj && q4 + u < j);
-          }
-          const bool sel = j < M0 && rank < P;
-          const uint64_t msk = __ballot(sel);
-          if (sel) {
-            const int pos = before + __popcll(msk & ((1ull << lane) - 1ull));
-            sSel[wave * Pp + pos] = j;
-            if (topp && wave == 0) topp[((int64_t)bh * ntiles + tile) * P + pos] = j;
-          }
-          before += __popcll(msk);
+        int* gout = (topp && wave == 0) ? topp + ((int64_t)bh * ntiles + tile) * P : nullptr;
+        if (M0 <= 64) {
+          uint32_t u1[1] = {u[0]};
+          select_top<1>(u1, M0, P, lane, sSel + wave * Pp, gout);
+        } else if (M0 <= 128) {
+          uint32_t u2[2] = {u[0], u[1]};
+          select_top<2>(u2, M0, P, lane, sSel + wave * Pp, gout);
+        } else {
+          select_top<4>(u, M0, P, lane, sSel + wave * Pp, gout);
         }
         __builtin_amdgcn_wave_barrier();
       } else {
@@ -458,8 +510,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           for (int u = wave; u < nbk * KS; u += nw) {
             const int b = u / KS, s = u % KS;
             const int gs = cs + b * S + s_row;
-            const int row = (gs < P && c_row < C) ? M0 + sel[gs] * C + c_row : M0 + sel[0] * C;
-            lds_dma<BA>(cbh + (int64_t)row * D + s * 2 * E + E * hh, sCC + u * 64);
+            const bool ok = gs < P && c_row < C;
+            const in_t* src = cbh + (int64_t)(M0 + sel[ok ? gs : 0] * C + c_row) * D + s * 2 * E + E * hh;
+            lds_dma<BA>(ok ? (const void*)src : (const void*)zeros, sCC + u * 64);
           }
         }
         // value fragments: one DMA per (block, k-step, half, 64 dims); lane = dim
@@ -475,7 +528,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const int b = c >> 5, qq = c & 31;
           const int r = r_of_col(qq), hc = h_of_col(qq);
           const int gs = cs + b * S + 2 * (r / W) + hc, cc = r % W;
-          sNc[c] = (gs < P && cc < C) ? (float)nb[M0 + sel[gs] * C + cc] : 0.0f;
+          const float n = (gs < P && cc < C) ? (float)nb[M0 + sel[gs] * C + cc] : 0.0f;
+          sNc[c] = n;
+          sBc[c] = n > 0.0f ? 0.0f : -INFINITY;
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -491,12 +546,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             for (int s = 0; s < KS; ++s) cl[b] = T::mma_in(sCC[(b * KS + s) * 64 + lane], qf[s], cl[b]);
           }
         }
+        // stabiliser over the non-empty children (a -inf bias masks the rest);
+        // the logits themselves stay unmasked for Eq. 8
         float tm = -INFINITY;
 #pragma unroll
         for (int b = 0; b < NCB; ++b)
           if (b < nbk) {
+            const f32x4* bc = (const f32x4*)(sBc + b * 32 + 8 * hh);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, sNc[b * 32 + col_of(r, hh)] > 0.0f ? cl[b][r] : -INFINITY);
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 b4 = bc[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) tm = fmaxf(tm, cl[b][q * 4 + u] + b4[u]);
+            }
           }
         tm = xhalf_max(tm) * sl2;
         if (tm > m + kLazy) {
@@ -509,23 +571,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
         for (int b = 0; b < NCB; ++b) {
           if (b < nbk) {
+            const f32x4* nc = (const f32x4*)(sNc + b * 32 + 8 * hh);
+            const f32x4* bc = (const f32x4*)(sBc + b * 32 + 8 * hh);
 #pragma unroll
             for (int g2 = 0; g2 < 16 / W; ++g2) {
+              // Eq. 8: the parent logit is the mean of its C child logits; the
+              // W - C padding rows have zero codewords and add nothing.  A slot
+              // beyond P contributes nothing; an empty selected parent gets a
+              // bounded weight (its children carry zero values and counts).
               float sp = 0.0f;
 #pragma unroll
-              for (int c = 0; c < W; ++c)
-                if (c < C) sp += cl[b][g2 * W + c];
-              // a slot beyond P contributes nothing; an empty selected parent
-              // gets a bounded weight (its children carry zero values/counts)
+              for (int c = 0; c < W; ++c) sp += cl[b][g2 * W + c];
               const bool slot_ok = cs + b * S + 2 * g2 + hh < P;
               const float ap = slot_ok ? fast_exp2(fminf(fmaf(sp * invC, sl2, -m), kLazy + 1.0f)) : 0.0f;
 #pragma unroll
-              for (int c = 0; c < W; ++c) {
-                const float n = sNc[b * 32 + col_of(g2 * W + c, hh)];
-                const float e = n > 0.0f ? fast_exp2(fmaf(cl[b][g2 * W + c], sl2, -m)) : 0.0f;
-                const float da = (c < C) ? e - ap : 0.0f;
-                cl[b][g2 * W + c] = da;
-                zp = fmaf(da, n, zp);
+              for (int q = (g2 * W) / 4; q < (g2 * W + W) / 4; ++q) {
+                const f32x4 n4 = nc[(q >> 1) * 4 + (q & 1)];
+                const f32x4 b4 = bc[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                  // empty and padding children: weight 0 - ap against zero
+                  // values and counts, so they add exactly nothing
+                  const float da = fast_exp2(fmaf(cl[b][q * 4 + u] + b4[u], sl2, -m)) - ap;
+                  cl[b][q * 4 + u] = da;
+                  zp = fmaf(da, n4[u], zp);
+                }
               }
             }
 #pragma unroll
@@ -567,8 +637,8 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q)
   size_t b = (M0p <= 64 ? M0p * d * es : 0);  // parents' codeword fragments
   b += M0p * d * es;                          // parents' value fragments
   b += 2 * CH * d * es;                       // chunk codeword and value fragments
-  b += (M0p + CH) * 4;                        // counts
-  b += 2 * nw * M0p * 4;                      // importance partials and totals
+  b += 2 * (M0p + CH) * 4;                    // counts and biases
+  b += nw * M0p * 4;                          // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
   return b;
 }
@@ -596,7 +666,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
-  const size_t sig_bytes = align256((size_t)BH * 4);
+  const size_t sig_bytes = align256((size_t)BH * 4) + kZeroBytes;
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
   {
     const int parts = 4;
