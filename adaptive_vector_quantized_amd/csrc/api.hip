@@ -11,7 +11,6 @@
 
 namespace {
 
-constexpr int kAssignChunk = 512;    // keys per workgroup of the assignment kernel
 constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -59,12 +58,12 @@ int avq_assign_aggregate(const void* K, const void* V, const void* codebook, int
   if (!aligned16(vsum) || !aligned16(counts) || !aligned16(codebook) || (K && !aligned16(K)) ||
       (V && !aligned16(V)) || (assign && !aligned16(assign)))
     return AVQ_ERR_ALIGN;
-  if (avq::assign_smem_bytes(dtype, d, M0, C, kAssignChunk) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
+  if (avq::assign_smem_bytes(dtype, d, M0, C) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
   const int64_t Mt = (int64_t)M0 * (1 + C);
   hipStream_t st = (hipStream_t)stream;
   rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, counts, BH * Mt, st));
   if (rc != AVQ_OK || N == 0) return rc;
-  return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, kAssignChunk, vsum, counts,
+  return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, vsum, counts,
                                      assign, st));
 }
 

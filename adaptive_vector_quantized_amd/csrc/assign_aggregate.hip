@@ -5,19 +5,25 @@
 // One workgroup (4 waves) owns a chunk of consecutive keys of one (batch,
 // head).  Design for CDNA4:
 //   * Parent distances ||c||^2 - 2 k.c come from MFMA: parents of the head
-//     are staged once in LDS as the A operand, keys are streamed from HBM
-//     straight into B-operand registers (64 keys per wave step) and stay
-//     there for the child search.
+//     are staged once in LDS as the A operand (their norms are reduced from
+//     LDS), keys are streamed from HBM straight into B-operand registers (64
+//     keys per wave step) and stay there for the child search.
 //   * Child distances: the distinct parents of the wave's 64 keys are packed
-//     four (C <= 8) at a time into a 32-row block of their children, one MFMA
-//     block per group; each key then reads the C distances of its own parent
-//     from registers.  Parent and child distances use the same formula.
-//   * Aggregation without per-key global atomics: keys are counting-sorted in
-//     LDS by (parent, slot), then 8 streams walk the sorted keys with one lane
-//     per pair/quad of value dimensions, accumulate runs in registers and
-//     issue one coalesced atomic row update per run.  Counts are flushed from
-//     the LDS histogram.  Heavy-tailed occupancy therefore costs one atomic
-//     row update per chunk per codeword, not per key.
+//     S = 32 / W at a time into a 32-row block of their children, one MFMA
+//     block per group; the children's norms come from the same operand
+//     registers, so no codeword is read twice.  Each key then reads the C
+//     distances of its own parent from registers.
+//   * Aggregation without per-key atomics: the codewords the chunk touches
+//     get compact slots; every wave loads the values of its own keys in
+//     natural (coalesced) order straight into registers, issued right after
+//     the assignment so their latency overlaps the slot bookkeeping.  The
+//     value sums are then a matrix product on MFMA, (one-hot key -> slot)^T
+//     x V, 32 slots at a time: with one lane per value column and the keys
+//     of a lane half along K, the loaded registers already are the B
+//     operand.  The four waves' partial tiles are added in LDS and each
+//     touched codeword costs one coalesced atomic row update per chunk.
+#include <algorithm>
+
 #include "avq_device.h"
 #include "avq_launch.h"
 
@@ -25,68 +31,129 @@ namespace avq {
 
 namespace {
 
+// EPL consecutive input elements of one value row as they sit in registers
+template <class T, int EPL>
+struct RawV;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+template <>
+struct RawV<TBF16, 2> { using t = uint32_t; };
+template <>
+struct RawV<TBF16, 4> { using t = u32x2; };
+template <>
+struct RawV<TF32, 2> { using t = f32x2; };
+template <>
+struct RawV<TF32, 4> { using t = f32x4; };
+
+// Raw buffer load (bounds-checked by the descriptor: reads past num_records
+// return zero).  Word 3 of the descriptor is the gfx9-family raw-access value.
+// voff: per-lane byte offset, soff: wave-uniform byte offset.
+template <class R>
+__device__ __forceinline__ R buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  if constexpr (sizeof(R) == 4)
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+  else if constexpr (sizeof(R) == 8)
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+  else
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+constexpr int kBufWord3 = 0x00020000;
+
 template <class T>
-struct VecLoad;
-template <>
-struct VecLoad<TBF16> {
-  // EPL consecutive bf16 values -> float
-  template <int EPL>
-  __device__ static inline void load(const __bf16* p, float* out) {
-    if constexpr (EPL == 2) {
-      uint32_t u = *(const uint32_t*)p;
-      out[0] = __uint_as_float(u << 16);
-      out[1] = __uint_as_float(u & 0xFFFF0000u);
-    } else {
-      uint2 u = *(const uint2*)p;
-      out[0] = __uint_as_float(u.x << 16);
-      out[1] = __uint_as_float(u.x & 0xFFFF0000u);
-      out[2] = __uint_as_float(u.y << 16);
-      out[3] = __uint_as_float(u.y & 0xFFFF0000u);
-    }
-  }
-};
-template <>
-struct VecLoad<TF32> {
-  template <int EPL>
-  __device__ static inline void load(const float* p, float* out) {
-    if constexpr (EPL == 2) {
-      f32x2 v = *(const f32x2*)p;
-      out[0] = v[0];
-      out[1] = v[1];
-    } else {
-      f32x4 v = *(const f32x4*)p;
+__device__ __forceinline__ float frag_sumsq(typename T::frag_t v, float acc) {
+  if constexpr (T::E == 1) {
+    const float x = T::to_f32(v);
+    return fmaf(x, x, acc);
+  } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[i] = v[i];
+    for (int j = 0; j < T::E; ++j) {
+      const float x = T::to_f32(v[j]);
+      acc = fmaf(x, x, acc);
     }
+    return acc;
   }
-};
+}
 
 }  // namespace
 
+// LDS layout of one workgroup (byte offsets; every array 16-byte aligned)
+struct AssignLds {
+  unsigned par, norm, cn, list, hist, scan, slot, row, bin, ks, acc, total;
+};
+
+static size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+template <class T, int D>
+struct AssignShape {
+  static constexpr int EPL = D / 32;  // value elements per lane (32 lanes per key)
+  static constexpr int kVgprPerKey = EPL * (int)sizeof(typename T::in_t) / 4;
+  static constexpr int KPW = 128 / kVgprPerKey;  // keys per wave: 64 registers of values
+  static constexpr int kChunk = 4 * KPW;         // keys per workgroup
+  static constexpr int LDP = D + 16 / (int)sizeof(typename T::in_t);  // padded LDS row of a parent
+  static constexpr int kWaves = (D == 64 && T::E > 1) ? 4 : 2;  // waves per SIMD the registers are set for
+};
+
+static AssignLds assign_lds(int es, int d, int M0, int C, int chunk) {
+  const size_t M0p = (M0 + 31) & ~31;
+  const size_t Mt = (size_t)M0 * (1 + C);
+  const size_t NB = (size_t)M0 * (C + 1);
+  const size_t ldp = d + 16 / es;
+  size_t o = 0, at[12];
+  // assignment phase only
+  at[0] = o; o = al16(o + M0p * ldp * es);         // parents, padded rows
+  at[1] = o; o = al16(o + M0p * 4);                // parent norms
+  at[2] = o; o = al16(o + 4 * 32 * 4);             // child-block norms, per wave
+  at[3] = o; o = al16(o + 4 * 64 * 4);             // distinct parents of a wave step
+  // aggregation phase only: four partial value tiles over the same bytes
+  at[9] = 0;
+  o = std::max(o, al16((size_t)4 * 32 * d * 4));
+  at[4] = o; o = al16(o + NB * 4);                 // key count per (parent, child slot)
+  at[5] = o; o = al16(o + 8 * 4);                  // scan partials
+  at[6] = o; o = al16(o + Mt * 2);                 // codeword -> slot
+  at[7] = o; o = al16(o + Mt * 2);                 // slot -> codeword
+  at[8] = o; o = al16(o + (size_t)chunk * 2);      // parent << 8 | child slot of every key
+  at[11] = o; o = al16(o + (size_t)chunk * 4);     // parent slot | child slot << 16 of every key
+  at[10] = o;
+  AssignLds L;
+  L.par = (unsigned)at[0]; L.norm = (unsigned)at[1]; L.cn = (unsigned)at[2]; L.list = (unsigned)at[3];
+  L.hist = (unsigned)at[4]; L.scan = (unsigned)at[5]; L.slot = (unsigned)at[6]; L.row = (unsigned)at[7];
+  L.bin = (unsigned)at[8]; L.ks = (unsigned)at[11]; L.acc = (unsigned)at[9]; L.total = (unsigned)at[10];
+  return L;
+}
+
 // W: width of a child slot in accumulator registers (C <= W, W in {4,8,16}).
 template <class T, int D, int W>
-__global__ __launch_bounds__(256) void assign_aggregate_kernel(
-    const typename T::in_t* __restrict__ K, const typename T::in_t* __restrict__ V,
-    const typename T::in_t* __restrict__ cb, int H, int N, int M0, int C, int chunk,
-    float* __restrict__ vsum, int* __restrict__ counts, int* __restrict__ assign) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AssignShape<T, D>::kWaves))) void
+assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T::in_t* __restrict__ V,
+                        const typename T::in_t* __restrict__ cb, int H, int N, int M0, int C,
+                        AssignLds L, float* __restrict__ vsum, int* __restrict__ counts, int* __restrict__ assign) {
   using in_t = typename T::in_t;
   using frag_t = typename T::frag_t;
+  using Sh = AssignShape<T, D>;
+  using raw_t = typename RawV<T, Sh::EPL>::t;
   constexpr int E = T::E;
-  constexpr int KS = D / (2 * E);            // k-steps over the head dimension
-  constexpr int LDP = D + 16 / sizeof(in_t); // padded LDS row of a parent
-  constexpr int S = 32 / W;                  // child slots per 32-row block
-  constexpr int EPL = D / 32;                // value elements per lane in the walk
+  constexpr int KS = D / (2 * E);  // k-steps over the head dimension
+  constexpr int LDP = Sh::LDP;
+  constexpr int S = 32 / W;        // child slots per 32-row block
+  constexpr int EPL = Sh::EPL;
+  constexpr int KPW = Sh::KPW;
+  constexpr int chunk = Sh::kChunk;
 
   extern __shared__ __align__(16) unsigned char smem[];
   const int Mt = M0 * (1 + C);
   const int M0p = (M0 + 31) & ~31;
   const int NB = M0 * (C + 1);
-  in_t* sPar = (in_t*)smem;
-  float* sNorm = (float*)(sPar + (size_t)M0p * LDP);
-  int* sHist = (int*)(sNorm + Mt);
-  int* sScan = sHist + NB;
-  unsigned short* sBin = (unsigned short*)(sScan + 8);
-  unsigned short* sSorted = sBin + chunk;
+  in_t* sPar = (in_t*)(smem + L.par);
+  float* sNorm = (float*)(smem + L.norm);
+  float* sCN = (float*)(smem + L.cn);
+  int* sList = (int*)(smem + L.list);
+  int* sHist = (int*)(smem + L.hist);
+  int* sScan = (int*)(smem + L.scan);
+  unsigned short* sSlot = (unsigned short*)(smem + L.slot);
+  unsigned short* sRow = (unsigned short*)(smem + L.row);
+  unsigned short* sBin = (unsigned short*)(smem + L.bin);
+  uint32_t* sKS = (uint32_t*)(smem + L.ks);
+  float* sAcc = (float*)(smem + L.acc);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -98,48 +165,43 @@ __global__ __launch_bounds__(256) void assign_aggregate_kernel(
   const in_t* Kb = K + (int64_t)bh * N * D;
   const in_t* Vb = V + (int64_t)bh * N * D;
 
-  // ---- stage parents, codeword norms, clear the histogram ---------------
+  // ---- stage parents, clear the histogram, parent norms from LDS ---------
   for (int i = tid; i < M0p * (D / E); i += 256) {
     const int row = i / (D / E), col = (i % (D / E)) * E;
     const int src = row < M0 ? row : 0;
-    frag_t v = *(const frag_t*)(cbh + (int64_t)src * D + col);
-    *(frag_t*)(sPar + row * LDP + col) = v;
-  }
-  for (int r = tid; r < Mt; r += 256) {
-    const frag_t* c = (const frag_t*)(cbh + (int64_t)r * D);
-    float acc = 0.0f;
-    for (int t = 0; t < D / E; ++t) {
-      frag_t v = c[t];
-      if constexpr (E == 1) {
-        float x = T::to_f32(v);
-        acc = fmaf(x, x, acc);
-      } else {
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          float x = T::to_f32(v[j]);
-          acc = fmaf(x, x, acc);
-        }
-      }
-    }
-    sNorm[r] = acc;
+    *(frag_t*)(sPar + row * LDP + col) = *(const frag_t*)(cbh + (int64_t)src * D + col);
   }
   for (int i = tid; i < NB; i += 256) sHist[i] = 0;
   __syncthreads();
+  for (int i = tid; i < M0p * 4; i += 256) {  // 4 lanes per row; M0p * 4 is a multiple of 64
+    const int row = i >> 2, q = i & 3;
+    const in_t* pr = sPar + row * LDP + q * (D / 4);
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < D / 4; t += E) acc = frag_sumsq<T>(*(const frag_t*)(pr + t), acc);
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (q == 0) sNorm[row] = row < M0 ? acc : INFINITY;
+  }
+  __syncthreads();
 
   // ---- assignment, 64 keys per wave step ---------------------------------
-  const int keys_per_wave = chunk / 4;
   const int nblkP = M0p / 32;
-  for (int it = 0; it < keys_per_wave; it += 64) {
-    const int kbase = cstart + wave * keys_per_wave + it;
-    if (kbase >= N) break;
+  const int rr = r_of_row(ql), hr = h_of_row(ql);
+  const int srow = 2 * (rr / W) + hr, crow = rr % W;  // slot and child of this lane's A row
+  int* list = sList + wave * 64;
+  float* cn = sCN + wave * 32;
+  for (int it = 0; it < KPW; it += 64) {
+    const int kloc = wave * KPW + it;  // first key of the step, chunk-relative
+    if (kloc >= nval) break;
     frag_t kf[2][KS];
     int key[2];
     bool kval[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      key[g] = kbase + g * 32 + ql;
-      kval[g] = key[g] < N;
-      const in_t* kp = Kb + (int64_t)(kval[g] ? key[g] : N - 1) * D + E * hh;
+      key[g] = cstart + kloc + g * 32 + ql;
+      kval[g] = it + g * 32 + ql < KPW && kloc + g * 32 + ql < nval;
+      const in_t* kp = Kb + (int64_t)(kval[g] ? key[g] : cstart) * D + E * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) kf[g][s] = *(const frag_t*)(kp + s * 2 * E);
     }
@@ -158,7 +220,7 @@ __global__ __launch_bounds__(256) void assign_aggregate_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = blk * 32 + row_of(r, hh);
-        const float nrm = row < M0 ? sNorm[row] : INFINITY;
+        const float nrm = sNorm[row];
         const float d0 = nrm - 2.0f * a0[r];
         const float d1 = nrm - 2.0f * a1[r];
         if (d0 < best[0]) { best[0] = d0; bidx[0] = row; }
@@ -172,59 +234,65 @@ __global__ __launch_bounds__(256) void assign_aggregate_kernel(
       if (pb < best[g] || (pb == best[g] && pi < bidx[g])) { best[g] = pb; bidx[g] = pi; }
     }
 
-    // children of the distinct parents, S parents per MFMA block
-    float dch[2] = {INFINITY, INFINITY};
-    int cst[2] = {-1, -1};
-    bool need0 = kval[0], need1 = kval[1];
-    const int rr = r_of_row(ql), hr = h_of_row(ql);
-    const int srow = 2 * (rr / W) + hr, crow = rr % W;  // slot and child of this lane's A row
-    while (true) {
-      uint64_t b0 = __ballot(need0), b1 = __ballot(need1);
-      if ((b0 | b1) == 0) break;
-      int gpar[S];
-      int ng = 0, slot0 = -1, slot1 = -1;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        gpar[s] = -1;
-        b0 = __ballot(need0);
-        b1 = __ballot(need1);
+    // distinct parents of the step, in order of first appearance
+    int idx[2] = {-1, -1};
+    int n = 0;
+    {
+      bool need0 = kval[0], need1 = kval[1];
+      while (true) {
+        const uint64_t b0 = __ballot(need0), b1 = __ballot(need1);
         if ((b0 | b1) == 0) break;
         const int p = b0 ? __builtin_amdgcn_readlane(bidx[0], __builtin_ctzll(b0))
                          : __builtin_amdgcn_readlane(bidx[1], __builtin_ctzll(b1));
-        gpar[s] = p;
-        ng = s + 1;
-        if (need0 && bidx[0] == p) { slot0 = s; need0 = false; }
-        if (need1 && bidx[1] == p) { slot1 = s; need1 = false; }
+        if (need0 && bidx[0] == p) { idx[0] = n; need0 = false; }
+        if (need1 && bidx[1] == p) { idx[1] = n; need1 = false; }
+        if (lane == 0) list[n] = p;
+        ++n;
       }
-      int prow = -1;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        if (s == srow && s < ng) prow = gpar[s];
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // children of S distinct parents per MFMA block; their norms from the
+    // same operand registers
+    float dch[2] = {INFINITY, INFINITY};
+    int cst[2] = {-1, -1};
+    const int nblkC = (n + S - 1) / S;
+    for (int blk = 0; blk < nblkC; ++blk) {
+      const int li = blk * S + srow;
+      const int prow = li < n ? list[li] : -1;
       const int crow_idx = (prow >= 0 && crow < C) ? M0 + prow * C + crow : 0;
       const in_t* cp = cbh + (int64_t)crow_idx * D + E * hh;
+      frag_t a[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[s] = *(const frag_t*)(cp + s * 2 * E);
+      float nrm = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) nrm = frag_sumsq<T>(a[s], nrm);
+      nrm += xhalf_partner(nrm);
+      if (hh == 0) cn[ql] = nrm;
       f32x16 c0 = zero16(), c1 = zero16();
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        frag_t a = *(const frag_t*)(cp + s * 2 * E);
-        c0 = T::mma_in(a, kf[0][s], c0);
-        c1 = T::mma_in(a, kf[1][s], c1);
+        c0 = T::mma_in(a[s], kf[0][s], c0);
+        c1 = T::mma_in(a[s], kf[1][s], c1);
       }
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const int slot = g ? slot1 : slot0;
-        if (slot >= 0 && (slot & 1) == hh) {
-          const int gg = slot >> 1;
-          const int base = M0 + bidx[g] * C;
+        const int sl = idx[g] - blk * S;
+        if (sl >= 0 && sl < S && (sl & 1) == hh) {
+          const int gg = sl >> 1;
           float dmin = INFINITY;
           int cmin = -1;
 #pragma unroll
           for (int c = 0; c < W; ++c) {
             if (c < C) {
               float v = g ? c1[c] : c0[c];
+              int r = c;
 #pragma unroll
               for (int gi = 1; gi < 16 / W; ++gi)
-                if (gg == gi) v = g ? c1[gi * W + c] : c0[gi * W + c];
-              const float dist = sNorm[base + c] - 2.0f * v;
+                if (gg == gi) { v = g ? c1[gi * W + c] : c0[gi * W + c]; r = gi * W + c; }
+              const float dist = cn[row_of(r, hh)] - 2.0f * v;
               if (dist < dmin) { dmin = dist; cmin = c; }
             }
           }
@@ -232,6 +300,7 @@ __global__ __launch_bounds__(256) void assign_aggregate_kernel(
           cst[g] = cmin;
         }
       }
+      __builtin_amdgcn_wave_barrier();
     }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -247,112 +316,179 @@ __global__ __launch_bounds__(256) void assign_aggregate_kernel(
     const int k_ = hh ? key[1] : key[0];
     if (hh ? kval[1] : kval[0]) {
       const bool moved = cs_ >= 0 && dc_ < db_;
-      const int bin = a_ * (C + 1) + (moved ? 1 + cs_ : 0);
-      sBin[k_ - cstart] = (unsigned short)bin;
-      atomicAdd(&sHist[bin], 1);
+      const int sl = moved ? 1 + cs_ : 0;
+      sBin[k_ - cstart] = (unsigned short)((a_ << 8) | sl);
+      atomicAdd(&sHist[a_ * (C + 1) + sl], 1);
       if (assign) assign[(int64_t)bh * N + k_] = moved ? M0 + a_ * C + cs_ : a_;
     }
   }
+
+  // ---- values of this wave's keys into registers ------------------------
+  // Half hh of the wave owns the KH consecutive keys from seg0; lane ql of
+  // the half holds dims EPL*ql .. EPL*ql+EPL-1 of every one of them.  Keys
+  // past the end of the sequence read as zero (descriptor bound).
+  constexpr int KH = KPW / 2;
+  const int seg0 = wave * KPW + hh * KH;
+  raw_t vr[KH];
+  {
+    const int w0 = __builtin_amdgcn_readfirstlane(wave * KPW);
+    const int nk = __builtin_amdgcn_readfirstlane(max(0, min(KPW, nval - w0)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vb + (int64_t)(cstart + w0) * D), 0, nk * D * (int)sizeof(in_t), kBufWord3);
+    const int voff = (hh * KH * D + ql * EPL) * (int)sizeof(in_t);
+#pragma unroll
+    for (int u = 0; u < KH; ++u) vr[u] = buf_load<raw_t>(rs, voff, u * D * (int)sizeof(in_t));
+  }
   __syncthreads();
 
-  // ---- counts, and bin offsets for the counting sort ----------------------
-  // thread t owns parent t (M0 <= 256): bins t*(C+1) .. t*(C+1)+C
-  int mycount = 0;
+  // ---- slots: thread p owns parent p (M0 <= 256) and its C children -------
+  int nz = 0, pcount = 0;
   if (tid < M0) {
-    for (int sl = 0; sl <= C; ++sl) mycount += sHist[tid * (C + 1) + sl];
-    if (mycount > 0) {
-      atomicAdd(&counts[(int64_t)bh * Mt + tid], mycount);
-      for (int sl = 1; sl <= C; ++sl) {
-        const int c = sHist[tid * (C + 1) + sl];
-        if (c) atomicAdd(&counts[(int64_t)bh * Mt + M0 + tid * C + sl - 1], c);
-      }
+#pragma unroll 1
+    for (int sl = 0; sl <= C; ++sl) {
+      const int c = sHist[tid * (C + 1) + sl];
+      pcount += c;
+      nz += (sl > 0 && c > 0);
     }
+    nz += pcount > 0;
   }
-  const int incl = wave_incl_scan(mycount, lane);
+  const int incl = wave_incl_scan(nz, lane);
   if (lane == 63) sScan[wave] = incl;
   __syncthreads();
-  int off = incl - mycount;
-  for (int w = 0; w < wave; ++w) off += sScan[w];
-  if (tid < M0) {
-    for (int sl = 0; sl <= C; ++sl) {
-      const int b = tid * (C + 1) + sl;
-      const int c = sHist[b];
-      sHist[b] = off;
-      off += c;
+  int off = incl - nz;
+  int nslots = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    off += w < wave ? sScan[w] : 0;
+    nslots += sScan[w];
+  }
+  if (tid < M0 && pcount > 0) {
+    sSlot[tid] = (unsigned short)off;
+    sRow[off++] = (unsigned short)tid;
+#pragma unroll 1
+    for (int sl = 1; sl <= C; ++sl) {
+      if (sHist[tid * (C + 1) + sl] > 0) {
+        const int r = M0 + tid * C + sl - 1;
+        sSlot[r] = (unsigned short)off;
+        sRow[off++] = (unsigned short)r;
+      }
     }
   }
   __syncthreads();
+  // slots of every key: parent slot | child slot << 16 (0xFFFF: the key stayed)
   for (int k = tid; k < nval; k += 256) {
-    const int pos = atomicAdd(&sHist[sBin[k]], 1);
-    sSorted[pos] = (unsigned short)k;
+    const int x = sBin[k];
+    const int p = x >> 8, sl = x & 255;
+    const uint32_t cs = sl ? (uint32_t)sSlot[M0 + p * C + sl - 1] : 0xFFFFu;
+    sKS[k] = (uint32_t)sSlot[p] | (cs << 16);
   }
   __syncthreads();
 
-  // ---- value sums: 8 streams walk the sorted keys ---------------------------
-  const int stream = wave * 2 + hh;
-  const int per = (nval + 7) / 8;
-  const int p0 = stream * per;
-  const int p1 = min(nval, p0 + per);
-  const int col = ql * EPL;
-  float pacc[EPL], cacc[EPL];
+  // ---- value sums on MFMA: (one-hot of key -> slot)^T x V -------------------
+  // Slots are taken 32 at a time (M = slots).  K = keys: a k-step takes E
+  // keys of each half's segment (the A and B operands of lane (m/n, hh) both
+  // refer to segment hh), so the registers already hold B = V with keys along
+  // K, one block of N = 32 columns per value element i (dim EPL*n + i).  A
+  // key contributes to the slot of its parent and, if it moved, of its child.
+  // Each wave reduces its own keys; the four partial tiles meet in LDS and
+  // one atomic row update per touched codeword goes to HBM.
+  float* vsb = vsum + (int64_t)bh * Mt * D;
+  float* tile = sAcc;  // [4 waves][32 slots][D]
+  for (int sb = 0; sb * 32 < nslots; ++sb) {
+    f32x16 acc[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) { pacc[e] = 0.0f; cacc[e] = 0.0f; }
-  int pcur = -1, ccur = -1;
-  float* vsb = vsum + (int64_t)bh * Mt * D + col;
-  constexpr int U = 8;
-  for (int pos = p0; pos < p1; pos += U) {
-    float vb[U][EPL];
-    int bb[U];
+    for (int i = 0; i < EPL; ++i) acc[i] = zero16();
+    const uint32_t mslot = (uint32_t)(32 * sb + ql);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pp = pos + u;
-      const int k = sSorted[pp < p1 ? pp : p0];
-      bb[u] = pp < p1 ? (int)sBin[k] : -1;
-      VecLoad<T>::template load<EPL>(Vb + (int64_t)(cstart + k) * D + col, vb[u]);
-    }
+    for (int t = 0; t < KH / E; ++t) {
+      // slots of the E keys of this k-step (same for all lanes of a half)
+      uint32_t ks[E];
+      if constexpr (E == 8) {
+        const u32x4 k0 = *(const u32x4*)(sKS + seg0 + 8 * t);
+        const u32x4 k1 = *(const u32x4*)(sKS + seg0 + 8 * t + 4);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = bb[u];
-      if (b < 0) break;
-      const int p = b / (C + 1);
-      const int sl = b - p * (C + 1);
-      if (p != pcur) {
-        if (pcur >= 0) {
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) atomic_add_f32(vsb + (int64_t)pcur * D + e, pacc[e]);
-        }
-        pcur = p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) pacc[e] = 0.0f;
+        for (int j = 0; j < 4; ++j) { ks[j] = k0[j]; ks[4 + j] = k1[j]; }
+      } else {
+        ks[0] = sKS[seg0 + t];
       }
+      frag_t a;
+      if constexpr (E == 8) {
+        u32x4 w;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) pacc[e] += vb[u][e];
-      if (sl > 0) {
-        if (b != ccur) {
-          if (ccur >= 0) {
-            const int cp = ccur / (C + 1);
-            const int crow = M0 + cp * C + (ccur - cp * (C + 1)) - 1;
+        for (int q = 0; q < 4; ++q) {
+          uint32_t x = 0;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) atomic_add_f32(vsb + (int64_t)crow * D + e, cacc[e]);
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t kk = ks[2 * q + j];
+            const bool valid = seg0 + 8 * t + 2 * q + j < nval;
+            const bool hit = valid && ((kk & 0xFFFFu) == mslot || (kk >> 16) == mslot);
+            x |= hit ? (0x3F80u << (16 * j)) : 0u;  // bf16 1.0
           }
-          ccur = b;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) cacc[e] = 0.0f;
+          w[q] = x;
         }
+        a = __builtin_bit_cast(frag_t, w);
+      } else {
+        const uint32_t kk = ks[0];
+        const bool valid = seg0 + t < nval;
+        a = (valid && ((kk & 0xFFFFu) == mslot || (kk >> 16) == mslot)) ? 1.0f : 0.0f;
+      }
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) cacc[e] += vb[u][e];
+      for (int i = 0; i < EPL; ++i) {
+        frag_t b;
+        if constexpr (E == 8) {
+          // element i of E consecutive keys, two bf16 per dword
+          u32x4 w;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t lo, hi;
+            if constexpr (EPL == 2) {
+              lo = vr[8 * t + 2 * q];
+              hi = vr[8 * t + 2 * q + 1];
+            } else {
+              lo = vr[8 * t + 2 * q][i >> 1];
+              hi = vr[8 * t + 2 * q + 1][i >> 1];
+            }
+            w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+          }
+          b = __builtin_bit_cast(frag_t, w);
+        } else {
+          b = vr[t][i];
+        }
+        acc[i] = T::mma_in(a, b, acc[i]);
       }
     }
-  }
-  if (pcur >= 0) {
+    // partial tile of this wave: row = slot within the block, col = dim
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) atomic_add_f32(vsb + (int64_t)pcur * D + e, pacc[e]);
-  }
-  if (ccur >= 0) {
-    const int cp = ccur / (C + 1);
-    const int crow = M0 + cp * C + (ccur - cp * (C + 1)) - 1;
+    for (int r = 0; r < 16; ++r) {
+      float* tr = tile + (wave * 32 + row_of(r, hh)) * D + EPL * ql;
+      if constexpr (EPL == 2) {
+        *(f32x2*)tr = f32x2{acc[0][r], acc[1][r]};
+      } else {
+        *(f32x4*)tr = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      }
+    }
+    __syncthreads();
+    // one row per wave instruction: consecutive lanes, consecutive floats
+    const int nrow = min(32, nslots - 32 * sb);
+    for (int i = tid; i < nrow * D; i += 256) {
+      const int row = i / D, c = i % D;
+      float sum = tile[row * D + c];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) atomic_add_f32(vsb + (int64_t)crow * D + e, cacc[e]);
+      for (int w = 1; w < 4; ++w) sum += tile[(w * 32 + row) * D + c];
+      atomic_add_f32(vsb + (int64_t)sRow[32 * sb + row] * D + c, sum);
+    }
+    if ((sb + 1) * 32 < nslots) __syncthreads();  // the next block rewrites the tiles
+  }
+
+  // ---- counts --------------------------------------------------------------
+  if (tid < M0 && pcount > 0) {
+    int* cnt = counts + (int64_t)bh * Mt;
+    atomicAdd(&cnt[tid], pcount);
+#pragma unroll 1
+    for (int sl = 1; sl <= C; ++sl) {
+      const int c = sHist[tid * (C + 1) + sl];
+      if (c) atomicAdd(&cnt[M0 + tid * C + sl - 1], c);
+    }
   }
 }
 
@@ -363,34 +499,36 @@ __global__ __launch_bounds__(256) void zero_kernel(f32x4* __restrict__ a, int64_
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nb; i += stride) b[i] = 0;
 }
 
-size_t assign_smem_bytes(int dtype, int d, int M0, int C, int chunk) {
-  const size_t es = dtype == 0 ? 4 : 2;
-  const size_t ldp = d + 16 / es;
-  const size_t M0p = (M0 + 31) & ~31;
-  const size_t Mt = (size_t)M0 * (1 + C);
-  const size_t NB = (size_t)M0 * (C + 1);
-  return M0p * ldp * es + Mt * 4 + NB * 4 + 8 * 4 + (size_t)chunk * 2 * 2;
+template <class T, int D>
+static AssignLds lds_of(int M0, int C) {
+  return assign_lds((int)sizeof(typename T::in_t), D, M0, C, AssignShape<T, D>::kChunk);
+}
+
+size_t assign_smem_bytes(int dtype, int d, int M0, int C) {
+  if (dtype == 0) return d == 64 ? lds_of<TF32, 64>(M0, C).total : lds_of<TF32, 128>(M0, C).total;
+  return d == 64 ? lds_of<TBF16, 64>(M0, C).total : lds_of<TBF16, 128>(M0, C).total;
 }
 
 template <class T, int D, int W>
 static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, int BH, int H, int N, int M0, int C,
-                                  int chunk, float* vsum, int* counts, int* assign, hipStream_t st) {
-  const size_t smem = assign_smem_bytes(std::is_same<T, TF32>::value ? 0 : 1, D, M0, C, chunk);
+                                  float* vsum, int* counts, int* assign, hipStream_t st) {
+  using Sh = AssignShape<T, D>;
+  const AssignLds L = lds_of<T, D>(M0, C);
   auto kern = assign_aggregate_kernel<T, D, W>;
-  hipError_t e = raise_lds_limit((const void*)kern, smem);
+  hipError_t e = raise_lds_limit((const void*)kern, L.total);
   if (e != hipSuccess) return e;
-  dim3 grid((N + chunk - 1) / chunk, BH);
-  hipLaunchKernelGGL(kern, grid, dim3(256), smem, st, (const typename T::in_t*)K, (const typename T::in_t*)V,
-                     (const typename T::in_t*)cb, H, N, M0, C, chunk, vsum, counts, assign);
+  dim3 grid((N + Sh::kChunk - 1) / Sh::kChunk, BH);
+  hipLaunchKernelGGL(kern, grid, dim3(256), L.total, st, (const typename T::in_t*)K, (const typename T::in_t*)V,
+                     (const typename T::in_t*)cb, H, N, M0, C, L, vsum, counts, assign);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_assign_w(const void* K, const void* V, const void* cb, int BH, int H, int N, int M0, int C,
-                                  int chunk, float* vsum, int* counts, int* assign, hipStream_t st) {
-  if (C <= 4) return launch_assign_t<T, D, 4>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
-  if (C <= 8) return launch_assign_t<T, D, 8>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
-  return launch_assign_t<T, D, 16>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
+                                  float* vsum, int* counts, int* assign, hipStream_t st) {
+  if (C <= 4) return launch_assign_t<T, D, 4>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  if (C <= 8) return launch_assign_t<T, D, 8>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  return launch_assign_t<T, D, 16>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
 }
 
 hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st) {
@@ -403,13 +541,13 @@ hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStre
 }
 
 hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
-                         int C, int chunk, float* vsum, int* counts, int* assign, hipStream_t st) {
+                         int C, float* vsum, int* counts, int* assign, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_assign_w<TF32, 64>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
-    return launch_assign_w<TF32, 128>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
+    if (d == 64) return launch_assign_w<TF32, 64>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+    return launch_assign_w<TF32, 128>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
   }
-  if (d == 64) return launch_assign_w<TBF16, 64>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
-  return launch_assign_w<TBF16, 128>(K, V, cb, BH, H, N, M0, C, chunk, vsum, counts, assign, st);
+  if (d == 64) return launch_assign_w<TBF16, 64>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  return launch_assign_w<TBF16, 128>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
 }
 
 }  // namespace avq

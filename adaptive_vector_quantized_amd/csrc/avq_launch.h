@@ -12,7 +12,7 @@ namespace avq {
 // made once per size class, not on every launch.
 hipError_t raise_lds_limit(const void* kernel, size_t bytes);
 
-size_t assign_smem_bytes(int dtype, int d, int M0, int C, int chunk);
+size_t assign_smem_bytes(int dtype, int d, int M0, int C);
 size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q);
 
 // Children rows staged in LDS per chunk by the attention kernel.
@@ -23,7 +23,7 @@ struct AttnTraits {
 
 hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
-                         int C, int chunk, float* vsum, int* counts, int* assign, hipStream_t st);
+                         int C, float* vsum, int* counts, int* assign, hipStream_t st);
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH);
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
