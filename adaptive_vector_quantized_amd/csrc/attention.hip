@@ -169,8 +169,21 @@ __global__ __launch_bounds__(256) void attention_prep_kernel(const float* __rest
   const float* vs = vsum + (int64_t)bh * Mt * D;
   float sig = 1.0f;
   if constexpr (T::kScaleValues) {
+    // every block of the head forms the maximum itself (the head's sums are
+    // a few hundred KB, read from L2), 12 loads in flight per thread
+    constexpr int U = 12;
+    const int n4 = Mt * (D / 4);
     float mx = 0.0f;
-    for (int i = tid; i < Mt * (D / 4); i += 256) mx = fmaxf(mx, absmax4(((const f32x4*)vs)[i]));
+    for (int i0 = tid; i0 < n4; i0 += 256 * U) {
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * 256;
+        v[u] = ((const f32x4*)vs)[i < n4 ? i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, absmax4(v[u]));
+    }
     mx = wave_max(mx);
     if (lane == 0) red[wave] = mx;
     __syncthreads();
@@ -669,7 +682,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   const size_t sig_bytes = align256((size_t)BH * 4) + kZeroBytes;
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
   {
-    const int parts = 4;
+    const int parts = 8;
     hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(256), 0, st, vsum, M0, C, parts,
                        (unsigned char*)ws, sig_bytes, per_bh);
     hipError_t e = hipGetLastError();
