@@ -27,7 +27,21 @@
  *   counts     [B*H][Mt]        key counts (Eq. 3)
  *   query tiles: tile t of a head holds queries t*bq ... min(N, (t+1)*bq)-1
  *
- * Parity status of each function is listed in the oracle/README.md header.
+ * Pins (tests/oracle_pins.py checks each function against what the paper and
+ * the mathematics fix, not against itself):
+ *   avqo_assign               generator ground truth, keys equal to codewords,
+ *                             hand-built ties, brute force on small inputs
+ *   avqo_aggregate            column sums, parent/child count relations
+ *   avqo_importance(_f64)     two-parent closed form; w >= 0, w = 0 iff n = 0,
+ *                             sum of w over a tile = its query count
+ *   avqo_select               hand cases with ties, brute-force sort
+ *   avqo_attention_*          the three output forms agree; keys = parents and
+ *                             keys = children give exact softmax; linearity,
+ *                             convex hull; far-away empty child changes nothing
+ *   avqo_exact_attention      equal keys, a two-key closed form, keys = parents
+ *   avqo_key_margins,
+ *   avqo_tile_margin(s)       hand-computed tie distances
+ * No function is left unpinned.
  */
 #include <math.h>
 #include <stdint.h>

@@ -315,6 +315,73 @@ def pin_parent_logit_recovery():
         assert lhs == rhs
 
 
+def pin_exact_attention(lib):
+    """Eq. 1 on cases with a closed form: all keys equal gives the mean of V;
+    two keys give e^a v1 + e^b v2 over e^a + e^b; keys that are exactly the
+    parents equal the substituted-codebook form (an independent function); a
+    query sub-range returns the same rows as the full call."""
+    rng = np.random.default_rng(5)
+    N, d = 7, 4
+    Q = rng.standard_normal((1, N, d))
+    V = rng.standard_normal((1, N, d))
+    K = np.repeat(rng.standard_normal((1, 1, d)), N, axis=1)
+    o = _O(lib, 1, 1, N, d, 1, 1)
+    np.testing.assert_allclose(o.exact_attention(Q, K, V, 0.7), np.repeat(V.mean(axis=1, keepdims=True), N, 1),
+                               rtol=0, atol=1e-14)
+    # two keys, one query: logits a and b with scale 0.5
+    a, b = 0.9, -0.3
+    K2 = np.array([[[2.0, 0.0], [0.0, 2.0]]])
+    Q2 = np.array([[[a, b], [a, b]]])
+    V2 = np.array([[[1.0, -2.0], [3.0, 0.5]]])
+    y = (np.exp(a) * V2[0, 0] + np.exp(b) * V2[0, 1]) / (np.exp(a) + np.exp(b))
+    out = _O(lib, 1, 1, 2, 2, 1, 1).exact_attention(Q2, K2, V2, 0.5)
+    np.testing.assert_allclose(out[0, 0], y, rtol=1e-14)
+    # keys exactly the parents: quantized attention is exact (Eq. 1 = Eq. 4)
+    cfg, data = _small_case(33, M0=8, C=3, d=8)
+    cb = data["codebook"]
+    H, M0, d = cfg.H, cfg.M0, cfg.d
+    Kp = np.stack([cb[h][:M0] for h in range(H)])
+    Vp = rng.standard_normal((H, M0, d))
+    Qp = rng.standard_normal((H, M0, d))
+    op = _O(lib, 1, H, M0, d, M0, cfg.C)
+    ex = op.exact_attention(Qp, Kp, Vp, 0.5)
+    sub = op.forward(Qp, Kp, Vp, cb, 3, 4, 0.5, forms=("substituted",))["Y"]
+    np.testing.assert_allclose(ex, sub, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(op.exact_attention(Qp, Kp, Vp, 0.5, 2, 5), ex[:, 2:5], rtol=0, atol=0)
+
+
+def pin_margins(lib):
+    """The tie distances used to draw inputs, on hand cases: a key at (0.5, 0)
+    with parents at (0, 0) and (2, 0) has parent gap (2.25 - 0.25) / (1 +
+    0.25); a child at the same distance as the parent is a tie (margin 0); a
+    closer child gives |0.04 - 0.25| / 1.25.  Two parents, one query, P = 1:
+    the importance margin is w1 - w2 = (3e^a - 5e^b) / (3e^a + 5e^b)."""
+    d, M0, C = 2, 2, 2
+    cb = np.zeros((1, M0 * (1 + C), d))
+    cb[0, :2] = [[0, 0], [2, 0]]
+    cb[0, 2:4] = [[0, 1], [0.5, 0.5]]   # children of parent 0
+    cb[0, 4:6] = [[2, 1], [2, -1]]      # children of parent 1
+    K = np.array([[[0.5, 0.0]]])
+    o = _O(lib, 1, 1, 1, d, M0, C)
+    assert abs(o.key_margins(K, cb)[0, 0]) < 1e-15
+    cb[0, 3] = [0.5, 0.2]
+    np.testing.assert_allclose(o.key_margins(K, cb)[0, 0], 0.21 / 1.25, rtol=1e-13)
+    cb[0, 3] = [0.5, 3.0]               # both children far: the parent gap decides
+    cb[0, 2] = [0.5, 2.0]
+    np.testing.assert_allclose(o.key_margins(K, cb)[0, 0], min(2.0, 3.75, 5.0) / 1.25, rtol=1e-13)
+    # importance margin
+    d, M0, C = 2, 3, 1
+    cb = np.zeros((1, M0 * (1 + C), d))
+    cb[0, :M0] = [[1, 0], [0, 1], [1, 1]]
+    cb[0, M0:] = cb[0, :M0]
+    counts = np.array([[3, 5, 0, 0, 0, 0]], np.int32)
+    a, b = 0.7, -0.4
+    Q = np.array([[[2 * a, 2 * b]]])
+    m = _O(lib, 1, 1, 1, d, M0, C).tile_margins(Q, cb, counts, 1, 1, 0.5)
+    w1 = 3 * np.exp(a) / (3 * np.exp(a) + 5 * np.exp(b))
+    np.testing.assert_allclose(m[0, 0], abs(2 * w1 - 1), rtol=1e-12)
+
+
 PINS = {
     "assign_ground_truth": pin_assign_ground_truth,
     "assign_copies": pin_assign_copies,
@@ -329,4 +396,6 @@ PINS = {
     "keys_are_children": pin_keys_are_children,
     "linearity_and_hull": pin_linearity_and_hull,
     "empty_child_far_away": pin_empty_child_far_away,
+    "exact_attention": pin_exact_attention,
+    "margins": pin_margins,
 }
