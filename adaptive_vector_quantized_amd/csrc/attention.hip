@@ -37,6 +37,8 @@
 //
 // Children of a selected parent occupy W (8 or 16) consecutive accumulator
 // registers of one lane half, so S = 32 / W parents share a 32-row block.
+#include <algorithm>
+
 #include "avq_device.h"
 #include "avq_launch.h"
 
@@ -145,6 +147,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&u)[NG], int M0, int 
 // A fragment is E consecutive operand elements (8 fp16, or 1 fp32).
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kZeroBytes = 256;
+constexpr int kYRow = 68;  // floats per staged output row (64 dims + 4 to spread LDS banks)
 
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   const size_t pes = dtype == 0 ? 4 : 2;
@@ -154,70 +157,90 @@ size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   return align256((size_t)BH * 4) + kZeroBytes + (size_t)BH * per;
 }
 
+// Prep: one round of loads per thread.  Every block of a (batch, head) first
+// issues the gathers of its own fragments (at most kPrepFrag per thread) and
+// its share of the head's maximum, reduces the maximum, then scales, packs and
+// stores.  The blocks of a head each form the maximum themselves (the head's
+// value sums are a few hundred KB, read from L2), so no second launch and no
+// inter-block wait is needed.
+constexpr int kPrepThreads = 512;
+constexpr int kPrepFrag = 2;   // fragments per thread
+constexpr int kPrepMax = 18;   // f32x4 loads in flight per thread for the maximum
+
 template <class T, int D, int W>
-__global__ __launch_bounds__(256) void attention_prep_kernel(const float* __restrict__ vsum, int M0, int C, int parts,
-                                                             unsigned char* __restrict__ ws, size_t sig_bytes,
-                                                             size_t per_bh) {
+__global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const float* __restrict__ vsum, int M0, int C,
+                                                                      int parts, unsigned char* __restrict__ ws,
+                                                                      size_t sig_bytes, size_t per_bh) {
   using pvfrag_t = typename T::pvfrag_t;
   constexpr int E = T::E;
   constexpr int KV = 16 / E;
-  __shared__ float red[4];
+  constexpr int NWV = kPrepThreads / 64;
+  __shared__ float red[NWV];
   const int bh = blockIdx.x / parts, part = blockIdx.x % parts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Mt = M0 * (1 + C);
   const int M0p = (M0 + 31) & ~31;
   const float* vs = vsum + (int64_t)bh * Mt * D;
-  float sig = 1.0f;
-  if constexpr (T::kScaleValues) {
-    // every block of the head forms the maximum itself (the head's sums are
-    // a few hundred KB, read from L2), 12 loads in flight per thread
-    constexpr int U = 12;
-    const int n4 = Mt * (D / 4);
-    float mx = 0.0f;
-    for (int i0 = tid; i0 < n4; i0 += 256 * U) {
-      f32x4 v[U];
+  const int nP = (M0p / 32) * KV * 2 * D;  // parent fragments
+  const int nF = nP + M0 * (W / E) * D;    // + child fragments
+  // gathers of this thread's fragments (unscaled)
+  float x[kPrepFrag][E];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * 256;
-        v[u] = ((const f32x4*)vs)[i < n4 ? i : 0];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) mx = fmaxf(mx, absmax4(v[u]));
-    }
-    mx = wave_max(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    sig = value_scale(mx);
-  }
-  if (part == 0 && tid == 0) ((float*)ws)[bh] = sig;
-  if (blockIdx.x == 0 && tid < kZeroBytes / 4) ((float*)(ws + sig_bytes - kZeroBytes))[tid] = 0.0f;
-  const float inv = 1.0f / sig;
-  pvfrag_t* pf = (pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
-  const int nP = (M0p / 32) * KV * 2 * D;       // parent fragments
-  const int nC = M0 * (W / E) * D;              // child fragments
-  for (int f = part * 256 + tid; f < nP + nC; f += parts * 256) {
-    float x[E];
+  for (int k = 0; k < kPrepFrag; ++k) {
+    const int f = (k * parts + part) * kPrepThreads + tid;
     if (f < nP) {
       const int d = f % D, t = f / D;
-      const int hh = t % 2, bk = t / 2, k = bk % KV, b = bk / KV;
-      const int c0 = b * 32 + 16 * ((k * E) >> 3) + 8 * hh + ((k * E) & 7);
+      const int hh = t % 2, bk = t / 2, kk = bk % KV, b = bk / KV;
+      const int c0 = b * 32 + 16 * ((kk * E) >> 3) + 8 * hh + ((kk * E) & 7);
 #pragma unroll
       for (int j = 0; j < E; ++j) {
         const int p = parent_of_col(c0 + j);
-        x[j] = p < M0 ? vs[(int64_t)p * D + d] * inv : 0.0f;
+        x[k][j] = p < M0 ? vs[(int64_t)p * D + d] : 0.0f;
       }
-    } else {
+    } else if (f < nF) {
       const int g2 = f - nP;
       const int d = g2 % D, t = g2 / D;
       const int g = t % (W / E), p = t / (W / E);
 #pragma unroll
       for (int j = 0; j < E; ++j) {
         const int c = g * E + j;
-        x[j] = c < C ? vs[(int64_t)(M0 + p * C + c) * D + d] * inv : 0.0f;
+        x[k][j] = c < C ? vs[(int64_t)(M0 + p * C + c) * D + d] : 0.0f;
       }
     }
-    pf[f] = T::pack_pv(x);
+  }
+  float sig = 1.0f;
+  if constexpr (T::kScaleValues) {
+    const int n4 = Mt * (D / 4);
+    float mx = 0.0f;
+    for (int i0 = tid; i0 < n4; i0 += kPrepThreads * kPrepMax) {
+      f32x4 v[kPrepMax];
+#pragma unroll
+      for (int u = 0; u < kPrepMax; ++u) {
+        const int i = i0 + u * kPrepThreads;
+        v[u] = ((const f32x4*)vs)[i < n4 ? i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < kPrepMax; ++u) mx = fmaxf(mx, absmax4(v[u]));
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) mx = fmaxf(mx, red[w]);
+    sig = value_scale(mx);
+  }
+  if (part == 0 && tid == 0) ((float*)ws)[bh] = sig;
+  if (blockIdx.x == 0 && tid < kZeroBytes / 4) ((float*)(ws + sig_bytes - kZeroBytes))[tid] = 0.0f;
+  const float inv = 1.0f / sig;
+  pvfrag_t* pf = (pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
+#pragma unroll
+  for (int k = 0; k < kPrepFrag; ++k) {
+    const int f = (k * parts + part) * kPrepThreads + tid;
+    if (f < nF) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) x[k][j] *= inv;
+      pf[f] = T::pack_pv(x[k]);
+    }
   }
 }
 
@@ -262,6 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sW = sBc + CH;                                               // [nw][M0p]
   int* sSel = (int*)(sW + nw * M0p);                                  // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [1]
+  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 1) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -623,18 +647,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
     }
 
-    // Y = x / z (Alg. 2 line 20)
+    // Y = x / z (Alg. 2 line 20).  A lane holds 4-float runs of its query's
+    // row; the wave's 32 x 64 block goes through LDS so that every store
+    // instruction writes four whole rows (64 dims at a time).
     const float zt = xhalf_sum(zp);
-    if (qv) {
-      const float f = sig / zt;
-      float* yp = Yb + (int64_t)qi * D + 4 * hh;
+    const float f = qv ? sig / zt : 0.0f;
+    float* yw = sY + wave * 32 * kYRow;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int half = 0; half < DB / 2; ++half) {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int dbl = 0; dbl < 2; ++dbl)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f32x4 o = {xacc[db][4 * i] * f, xacc[db][4 * i + 1] * f, xacc[db][4 * i + 2] * f, xacc[db][4 * i + 3] * f};
-          *(f32x4*)(yp + db * 32 + 8 * i) = o;
+          const f32x16& a = xacc[2 * half + dbl];
+          const f32x4 o = {a[4 * i] * f, a[4 * i + 1] * f, a[4 * i + 2] * f, a[4 * i + 3] * f};
+          *(f32x4*)(yw + ql * kYRow + dbl * 32 + 8 * i + 4 * hh) = o;
         }
+      __builtin_amdgcn_wave_barrier();
+      const int q0 = tile * bq + wave * 32, r0 = lane >> 4, c4 = (lane & 15) * 4;
+      const float* src = yw + r0 * kYRow + c4;
+      float* dst = Yb + (int64_t)(q0 + r0) * D + half * 64 + c4;
+      if (q0 + 32 <= N) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (q0 + r0 + 4 * k < N) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
+      }
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qn[s];
@@ -653,6 +694,8 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q)
   b += 2 * (M0p + CH) * 4;                    // counts and biases
   b += nw * M0p * 4;                          // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
+  b = (b + 15) & ~(size_t)15;
+  b += nw * 32 * kYRow * 4;                   // output staging
   return b;
 }
 
@@ -682,9 +725,13 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   const size_t sig_bytes = align256((size_t)BH * 4) + kZeroBytes;
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
   {
-    const int parts = 8;
-    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(256), 0, st, vsum, M0, C, parts,
-                       (unsigned char*)ws, sig_bytes, per_bh);
+    constexpr int E = T::E, KV = 16 / E;
+    const int M0p = (M0 + 31) & ~31;
+    const int nF = (M0p / 32) * KV * 2 * D + M0 * (W / E) * D;
+    const int per_part = kPrepThreads * kPrepFrag;
+    const int parts = std::max(8, (nF + per_part - 1) / per_part);
+    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, M0, C,
+                       parts, (unsigned char*)ws, sig_bytes, per_bh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -18,7 +18,7 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q)
 // Children rows staged in LDS per chunk by the attention kernel.
 template <int D>
 struct AttnTraits {
-  static constexpr int kChunkRows = D == 64 ? 128 : 64;
+  static constexpr int kChunkRows = 64;
 };
 
 hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st);
