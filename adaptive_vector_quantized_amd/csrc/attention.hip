@@ -168,15 +168,28 @@ constexpr int kPrepFrag = 2;   // fragments per thread
 constexpr int kPrepMax = 18;   // f32x4 loads in flight per thread for the maximum
 
 template <class T, int D, int W>
-__global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const float* __restrict__ vsum, int M0, int C,
-                                                                      int parts, unsigned char* __restrict__ ws,
+__global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const float* __restrict__ vsum, int BH, int M0,
+                                                                      int C, int parts, unsigned char* __restrict__ ws,
                                                                       size_t sig_bytes, size_t per_bh) {
   using pvfrag_t = typename T::pvfrag_t;
   constexpr int E = T::E;
   constexpr int KV = 16 / E;
   constexpr int NWV = kPrepThreads / 64;
   __shared__ float red[NWV];
-  const int bh = blockIdx.x / parts, part = blockIdx.x % parts;
+  // the blocks of one (batch, head) on one XCD when possible (consecutive
+  // block ids go to the XCDs round robin): the head's sums are then read from
+  // HBM once and from that XCD's L2 afterwards
+  int bh, part;
+  {
+    const int L = blockIdx.x;
+    if ((BH & 7) == 0) {
+      bh = (L / (8 * parts)) * 8 + (L & 7);
+      part = (L >> 3) % parts;
+    } else {
+      bh = L / parts;
+      part = L % parts;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Mt = M0 * (1 + C);
   const int M0p = (M0 + 31) & ~31;
@@ -730,8 +743,8 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
     const int nF = (M0p / 32) * KV * 2 * D + M0 * (W / E) * D;
     const int per_part = kPrepThreads * kPrepFrag;
     const int parts = std::max(8, (nF + per_part - 1) / per_part);
-    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, M0, C,
-                       parts, (unsigned char*)ws, sig_bytes, per_bh);
+    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, BH, M0,
+                       C, parts, (unsigned char*)ws, sig_bytes, per_bh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
