@@ -295,7 +295,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sNc = sNp + M0p;                                             // [CH]
   float* sBp = sNc + CH;                                              // [M0p] 0 or -inf (empty)
   float* sBc = sBp + M0p;                                             // [CH]
-  float* sW = sBc + CH;                                               // [nw][M0p]
+  float* sNa = sBc + CH;                                              // [M0][W] counts of all children
+  float* sW = sNa + M0 * W;                                           // [nw][M0p]
   int* sSel = (int*)(sW + nw * M0p);                                  // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [1]
   float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 1) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
@@ -350,6 +351,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     sNp[c] = n;
     sBp[c] = n > 0.0f ? 0.0f : -INFINITY;
     if (j < M0 && !(n > 0.0f)) sFlag[0] = 0;
+  }
+  // counts of every child, slot-padded to W (the per-chunk staging then
+  // reads LDS, not global memory)
+  if (P > 0) {
+    for (int i = tid; i < M0 * W; i += nthreads) {
+      const int p = i / W, c = i % W;
+      sNa[i] = c < C ? (float)nb[M0 + p * C + c] : 0.0f;
+    }
   }
   frag_t qf[KS];
   {
@@ -578,7 +587,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const int b = c >> 5, qq = c & 31;
           const int r = r_of_col(qq), hc = h_of_col(qq);
           const int gs = cs + b * S + 2 * (r / W) + hc, cc = r % W;
-          const float n = (gs < P && cc < C) ? (float)nb[M0 + sel[gs] * C + cc] : 0.0f;
+          const float n = gs < P ? sNa[sel[gs] * W + cc] : 0.0f;
           sNc[c] = n;
           sBc[c] = n > 0.0f ? 0.0f : -INFINITY;
         }
@@ -705,6 +714,7 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q)
   b += M0p * d * es;                          // parents' value fragments
   b += 2 * CH * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + CH) * 4;                    // counts and biases
+  b += (size_t)M0 * (C <= 8 ? 8 : 16) * 4;    // counts of all children
   b += nw * M0p * 4;                          // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
   b = (b + 15) & ~(size_t)15;
