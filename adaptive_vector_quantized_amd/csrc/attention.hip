@@ -638,9 +638,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
               // W - C padding rows have zero codewords and add nothing.  A slot
               // beyond P contributes nothing; an empty selected parent gets a
               // bounded weight (its children carry zero values and counts).
-              float sp = 0.0f;
+              float sp = cl[b][g2 * W];
 #pragma unroll
-              for (int c = 0; c < W; ++c) sp += cl[b][g2 * W + c];
+              for (int c = 1; c < W; ++c) sp += cl[b][g2 * W + c];
               const bool slot_ok = cs + b * S + 2 * g2 + hh < P;
               const float ap = slot_ok ? fast_exp2(fminf(fmaf(sp * invC, sl2, -m), kLazy + 1.0f)) : 0.0f;
 #pragma unroll

@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of the AVQ-Attention forward pass on one MI355X.
 
-One step = one pass of the whole hot path over one batch: kernel 1
+One step = one pass of the whole hot path over one batch: call 1
 (avq_assign_aggregate: zero fill + two-level assignment + value sums and
-counts) then kernel 2 (avq_attention_fwd: parent attention, importance, top-P,
-child correction, output), both through the C interface, on synthetic inputs
-already resident in HBM.  Three input sets are rotated (larger than the
-256 MB Infinity Cache together) so that every step streams from HBM.
+counts) then call 2 (avq_attention_fwd: per-head fp16 value fragments, then
+parent attention, importance, top-P, child correction, output), both through
+the C interface, on synthetic inputs already resident in HBM.  Three input
+sets are rotated (larger than the 256 MB Infinity Cache together) so that
+every step streams from HBM.
 
 Prints one JSON line:
   value            tokens per second of the whole pass, in millions (B*N / step time)
-  roofline         the dominant kernel's algorithmic bytes per launch over its
-                   average duration (HIP events on the launch stream, inside the
-                   timed region) against MI355X's 8 TB/s HBM peak
-  kernels          the same figures for both kernels, with MFMA fractions
-  cpu_baseline     the CPU oracle on a bounded sample of the same workload
+  roofline         the dominant call's algorithmic bytes per call over its
+                   average duration (HIP events on the launch stream around the
+                   call, inside the timed region) against MI355X's 8 TB/s HBM
+                   peak; traffic = counter-measured HBM bytes per call
+  kernels          the same figures for both calls (and the kernels each
+                   launches), with MFMA fractions
+  cpu_baseline     the CPU oracle on the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grid128]
 """
@@ -36,17 +39,21 @@ METRIC = "AVQ fwd Mtokens/s at N=16384,H=16,d=64,M0=64,C=8,P=16; % HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_FP32_PEAK_TFLOPS = 157.3
-KERNEL_SOURCES = {
-    "assign_aggregate_kernel": ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
-                                "adaptive_vector_quantized_amd/csrc/avq_device.h"],
-    "attention_kernel": ["adaptive_vector_quantized_amd/csrc/attention.hip",
-                         "adaptive_vector_quantized_amd/csrc/avq_device.h"],
+# each timed unit is one C call; the kernels it launches, and their sources
+CALLS = {
+    "avq_assign_aggregate": ("zero_kernel + assign_aggregate_kernel",
+                             ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
+                              "adaptive_vector_quantized_amd/csrc/avq_device.h"]),
+    "avq_attention_fwd": ("attention_prep_kernel + attention_kernel",
+                          ["adaptive_vector_quantized_amd/csrc/attention.hip",
+                           "adaptive_vector_quantized_amd/csrc/avq_device.h",
+                           "adaptive_vector_quantized_amd/csrc/avq_launch.h"]),
 }
 
 
-def source_hash(kernel: str) -> str:
+def source_hash(call: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel]:
+    for rel in CALLS[call][1]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -68,18 +75,18 @@ def algorithmic(cfg, P):
     k2_bytes = BH * N * d * es + BH * N * d * 4 + cb + aggr
     k1_flops = 2.0 * d * (M0 + C) * BH * N
     k2_flops = 4.0 * d * (M0 + P * C) * BH * N
-    return {"assign_aggregate_kernel": (k1_bytes, k1_flops), "attention_kernel": (k2_bytes, k2_flops)}
+    return {"avq_assign_aggregate": (k1_bytes, k1_flops), "avq_attention_fwd": (k2_bytes, k2_flops)}
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+def load_traffic(call: str, workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{call}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != source_hash(kernel):
+    if rec.get("source_hash") != source_hash(call):
         return None
     return rec.get("bytes_per_launch")
 
@@ -195,10 +202,11 @@ def main():
     alg = algorithmic(cfg, P)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
     kernels = {}
-    for name, t in (("assign_aggregate_kernel", k1), ("attention_kernel", k2)):
+    for name, t in (("avq_assign_aggregate", k1), ("avq_attention_fwd", k2)):
         b, f = alg[name]
         avg = float(t.mean())
         kernels[name] = {
+            "launches": CALLS[name][0],
             "avg_us": avg * 1e6, "median_us": float(np.median(t)) * 1e6,
             "algorithmic_bytes": b, "algorithmic_flops": f,
             "GBps": b / avg / 1e9, "hbm_frac": b / avg / 1e9 / HBM_PEAK_GBS,
@@ -227,7 +235,7 @@ def main():
             "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "call": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kd["hbm_frac"], 4), "traffic": traffic,
         },
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
