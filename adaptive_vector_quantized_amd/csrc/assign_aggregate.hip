@@ -23,6 +23,7 @@
 //     operand.  The four waves' partial tiles are added in LDS and each
 //     touched codeword costs one coalesced atomic row update per chunk.
 #include <algorithm>
+#include <type_traits>
 
 #include "avq_device.h"
 #include "avq_launch.h"
@@ -394,44 +395,39 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // one atomic row update per touched codeword goes to HBM.
   float* vsb = vsum + (int64_t)bh * Mt * D;
   float* tile = sAcc;  // [4 waves][32 slots][D]
+  // one-hot A operand of the wave in LDS, over the bytes of its partial tile:
+  // [half][k-step][slot row][E keys] (bf16 1.0 or 0; fp32 for E = 1)
+  using oh_t = typename std::conditional<E == 8, unsigned short, float>::type;
+  oh_t* oh = (oh_t*)(tile + wave * 32 * D);
+  constexpr int OHN = 2 * KH * 32;  // entries
   for (int sb = 0; sb * 32 < nslots; ++sb) {
+    // clear, then every key marks the rows of its parent and child slots
+    for (int i = lane; i < OHN * (int)sizeof(oh_t) / 16; i += 64) ((u32x4*)oh)[i] = u32x4{0u, 0u, 0u, 0u};
+    __builtin_amdgcn_wave_barrier();
+    for (int kk = lane; kk < KPW; kk += 64) {
+      const int kl = wave * KPW + kk;
+      if (kl < nval) {
+        const uint32_t x = sKS[kl];
+        const int h2 = kk / KH, u = kk % KH;
+        const int base = ((h2 * (KH / E) + u / E) * 32) * E + u % E;
+        const oh_t one = E == 8 ? (oh_t)0x3F80 : (oh_t)1.0f;
+        const int ps = (int)(x & 0xFFFFu) - 32 * sb, cs = (int)(x >> 16) - 32 * sb;
+        if (ps >= 0 && ps < 32) oh[base + ps * E] = one;
+        if (cs >= 0 && cs < 32) oh[base + cs * E] = one;  // 0xFFFF (stayed) is never in range
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
     f32x16 acc[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[i] = zero16();
-    const uint32_t mslot = (uint32_t)(32 * sb + ql);
 #pragma unroll
     for (int t = 0; t < KH / E; ++t) {
-      // slots of the E keys of this k-step (same for all lanes of a half)
-      uint32_t ks[E];
-      if constexpr (E == 8) {
-        const u32x4 k0 = *(const u32x4*)(sKS + seg0 + 8 * t);
-        const u32x4 k1 = *(const u32x4*)(sKS + seg0 + 8 * t + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { ks[j] = k0[j]; ks[4 + j] = k1[j]; }
-      } else {
-        ks[0] = sKS[seg0 + t];
-      }
+      const oh_t* ap = oh + ((hh * (KH / E) + t) * 32 + ql) * E;
       frag_t a;
-      if constexpr (E == 8) {
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t x = 0;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint32_t kk = ks[2 * q + j];
-            const bool valid = seg0 + 8 * t + 2 * q + j < nval;
-            const bool hit = valid && ((kk & 0xFFFFu) == mslot || (kk >> 16) == mslot);
-            x |= hit ? (0x3F80u << (16 * j)) : 0u;  // bf16 1.0
-          }
-          w[q] = x;
-        }
-        a = __builtin_bit_cast(frag_t, w);
-      } else {
-        const uint32_t kk = ks[0];
-        const bool valid = seg0 + t < nval;
-        a = (valid && ((kk & 0xFFFFu) == mslot || (kk >> 16) == mslot)) ? 1.0f : 0.0f;
-      }
+      if constexpr (E == 8)
+        a = __builtin_bit_cast(frag_t, *(const u32x4*)ap);
+      else
+        a = *ap;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         frag_t b;
@@ -457,7 +453,9 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
         acc[i] = T::mma_in(a, b, acc[i]);
       }
     }
-    // partial tile of this wave: row = slot within the block, col = dim
+    // partial tile of this wave (over its one-hot operand): row = slot within
+    // the block, col = dim
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float* tr = tile + (wave * 32 + row_of(r, hh)) * D + EPL * ql;
