@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--P", type=int, default=None)
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the whole pass at every refinement budget of the workload (e.g. --workload sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -160,34 +162,57 @@ def main():
     print(f"[bench] {cfg.name}: {args.sets} input sets resident, warmup {args.warmup}, steps {args.steps}",
           file=sys.stderr, flush=True)
 
-    def step(s):
-        _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
-        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"],
-                           workspace=s["ws"])
-
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-
-    # timed region: per-kernel events on the launch stream inside every step
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        s = sets[i % len(sets)]
-        e = ev[i]
-        e[0].record(stream)
-        _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
-        e[1].record(stream)
-        _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale, Y=s["Y"],
-                           workspace=s["ws"])
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3  # seconds
-    k2 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    gpu_span = ev[0][0].elapsed_time(ev[-1][2]) * 1e-3
+
+    def timed(P, steps, warmup):
+        """Warm up, then time `steps` whole passes at refinement budget P: wall
+        time, and per-call durations from events on the launch stream."""
+        def step(s):
+            _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
+            _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
+                               Y=s["Y"], workspace=s["ws"])
+
+        for i in range(warmup):
+            step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            s = sets[i % len(sets)]
+            e = ev[i]
+            e[0].record(stream)
+            _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
+            e[1].record(stream)
+            _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
+                               Y=s["Y"], workspace=s["ws"])
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3  # seconds
+        k2 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+        span = ev[0][0].elapsed_time(ev[-1][2]) * 1e-3
+        return wall, k1, k2, span
+
+    if args.sweep:
+        # one line: the whole pass at every refinement budget of the workload
+        rows = []
+        for Ps in (cfg.sweep_P or (P,)):
+            wall, k1, k2, _ = timed(Ps, args.steps, args.warmup)
+            rows.append({"P": Ps, "value": round(cfg.B * cfg.N / (wall / args.steps) / 1e6, 3),
+                         "ms_per_step": round(wall / args.steps * 1e3, 5),
+                         "avq_assign_aggregate_us": round(float(k1.mean()) * 1e6, 2),
+                         "avq_attention_fwd_us": round(float(k2.mean()) * 1e6, 2)})
+            print(f"[bench] P={Ps}: {rows[-1]}", file=sys.stderr, flush=True)
+        print(json.dumps({"metric": "AVQ fwd Mtokens/s versus the refinement budget P", "unit": "Mtokens/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                          "dtype": cfg.dtype, "data": "synthetic",
+                          "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} M0={cfg.M0} "
+                                                 f"C={cfg.C} block_q={cfg.block_q}"},
+                          "sweep": rows}), flush=True)
+        return
+
+    wall, k1, k2, gpu_span = timed(P, args.steps, args.warmup)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
