@@ -18,7 +18,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int check_common(int B, int H, int N, int d, int M0, int C, int dtype) {
   if (dtype != AVQ_F32 && dtype != AVQ_BF16) return AVQ_ERR_DTYPE;
   if (B < 0 || H < 0 || N < 0) return AVQ_ERR_SHAPE;
-  if (d < 1 || M0 < 1 || C < 1) return AVQ_ERR_SHAPE;
+  if (d < 1 || M0 < 1 || C < 0) return AVQ_ERR_SHAPE;
   if (d != 64 && d != 128) return AVQ_ERR_UNSUPPORTED;
   if (M0 > 256 || C > 16) return AVQ_ERR_UNSUPPORTED;
   if ((int64_t)B * H > 65535) return AVQ_ERR_UNSUPPORTED;
@@ -77,7 +77,7 @@ int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, co
                       int32_t* topp, float* importance, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
-  if (P < 0 || P > M0) return AVQ_ERR_SHAPE;
+  if (P < 0 || P > M0 || (C == 0 && P > 0)) return AVQ_ERR_SHAPE;  // no children to refine with
   if (block_q != 32 && block_q != 64 && block_q != 128) return AVQ_ERR_UNSUPPORTED;
   if (!isfinite(scale) || !(scale > 0.0f)) return AVQ_ERR_SHAPE;
   const int64_t BH = (int64_t)B * H;

@@ -235,10 +235,11 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
       if (pb < best[g] || (pb == best[g] && pi < bidx[g])) { best[g] = pb; bidx[g] = pi; }
     }
 
-    // distinct parents of the step, in order of first appearance
+    // distinct parents of the step, in order of first appearance (none to
+    // look at when the codebook has no children)
     int idx[2] = {-1, -1};
     int n = 0;
-    {
+    if (C > 0) {
       bool need0 = kval[0], need1 = kval[1];
       while (true) {
         const uint64_t b0 = __ballot(need0), b1 = __ballot(need1);

@@ -95,6 +95,9 @@ CONFIGS = {
     # large parent codebook at d=128 on a 256x256 grid
     "grid256": Config("grid256", B=1, H=8, N=65536, d=128, M0=256, C=8, P=32, block_q=128,
                       dtype="bf16", grid=256, parents="zipf", seed=1003),
+    # flat codebook of 256 codewords (no children, plain VQ attention) at the headline shape
+    "flat256": Config("flat256", B=2, H=16, N=16384, d=64, M0=256, C=0, P=0, block_q=128,
+                      dtype="bf16", grid=128, parents="zipf", seed=1005),
     # refinement-budget sweep on the 128x128 grid, one batch
     "sweep": Config("sweep", B=1, H=16, N=16384, d=64, M0=64, C=8, P=16, block_q=128,
                     dtype="bf16", grid=128, parents="zipf", seed=1004, sweep_P=(0, 4, 16, 64)),

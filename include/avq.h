@@ -33,7 +33,10 @@
  * dtype: AVQ_F32 (float) or AVQ_BF16 (bfloat16) for Q, K, V and the codebook.
  * Value sums, counts and outputs are float / int32 in both cases.
  *
- * Supported sizes: d in {64, 128}; 1 <= M0 <= 256; 1 <= C <= 16;
+ * Supported sizes: d in {64, 128}; 1 <= M0 <= 256; 0 <= C <= 16.  C = 0 is a
+ * flat codebook of M0 codewords (plain VQ attention, the pages' fused flat-VQ
+ * baseline of Sec. 5): keys are assigned to the nearest codeword only, and
+ * the attention call then requires P = 0.
  * B, H, N >= 0 (any of them zero makes the call a no-op, except that
  * avq_assign_aggregate still zeroes vsum and counts when B*H > 0).
  * Every pointer argument must be 16-byte aligned.
@@ -126,7 +129,8 @@ size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C,
  *   codebook   in  [H, Mt, d]  dtype
  *   vsum       in  [BH, Mt, d] float  (from avq_assign_aggregate)
  *   counts     in  [BH, Mt]    int32  (from avq_assign_aggregate)
- *   P          0 <= P <= M0 (P = 0: plain VQ attention over the parents)
+ *   P          0 <= P <= M0 (P = 0: plain VQ attention over the parents);
+ *              P must be 0 when C = 0 (AVQ_ERR_SHAPE otherwise)
  *   block_q    query tile: 32, 64 or 128 (one wave of 64 lanes per 32 queries)
  *   scale      logit scale, > 0 (1/sqrt(d) in the usual convention, Sec. 3.1)
  *   Y          out [BH, N, d] float

@@ -225,7 +225,8 @@ int avqo_attention_alg2(int B, int H, int N, int d, int M0, int C,
                         const double* Q, const double* cb, const double* vsum,
                         const int32_t* counts, const int32_t* sel, int P,
                         int bq, double scale, double* Y) {
-    if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 1 || bq < 1 || P < 0 || P > M0) return ORACLE_ERR;
+    if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 0 || bq < 1 || P < 0 || P > M0) return ORACLE_ERR;
+    if (C == 0 && P > 0) return ORACLE_ERR; /* a flat codebook has no children to refine with */
     const int64_t Mt = mt_of(M0, C);
     const int BH = B * H, T = ntiles(N, bq);
 #pragma omp parallel for schedule(static)
@@ -292,7 +293,8 @@ int avqo_attention_substituted(int B, int H, int N, int d, int M0, int C,
                                const double* Q, const double* cb, const double* vsum,
                                const int32_t* counts, const int32_t* sel, int P,
                                int bq, double scale, double* Y) {
-    if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 1 || bq < 1 || P < 0 || P > M0) return ORACLE_ERR;
+    if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 0 || bq < 1 || P < 0 || P > M0) return ORACLE_ERR;
+    if (C == 0 && P > 0) return ORACLE_ERR; /* a flat codebook has no children to refine with */
     const int64_t Mt = mt_of(M0, C);
     const int BH = B * H, T = ntiles(N, bq);
     const int64_t Muse = M0 + (int64_t)P * C;

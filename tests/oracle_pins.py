@@ -382,6 +382,23 @@ def pin_margins(lib):
     np.testing.assert_allclose(m[0, 0], abs(2 * w1 - 1), rtol=1e-12)
 
 
+def pin_flat_codebook(lib):
+    """A flat codebook (C = 0, no children) is plain VQ attention over its
+    codewords, exactly what P = 0 gives with the same codewords as parents of
+    a two-level codebook: the parent choice and the parents' aggregates do not
+    depend on the children, and P = 0 never looks at them."""
+    cfg, data = _small_case(51, M0=6, C=3, d=8)
+    cb, H, M0, d = data["codebook"], cfg.H, cfg.M0, cfg.d
+    o2 = _O(lib, cfg.B, H, cfg.N, d, M0, cfg.C)
+    two = o2.forward(data["Q"], data["K"], data["V"], cb, 0, cfg.block_q, cfg.scale, forms=("substituted", "alg2"))
+    o1 = _O(lib, cfg.B, H, cfg.N, d, M0, 0)
+    flat_cb = np.ascontiguousarray(cb[:, :M0])
+    flat = o1.forward(data["Q"], data["K"], data["V"], flat_cb, 0, cfg.block_q, cfg.scale, forms=("substituted", "alg2"))
+    assert np.array_equal(flat["row"], two["parent"])
+    np.testing.assert_allclose(flat["Y"], two["Y"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(flat["Y_alg2"], two["Y"], rtol=0, atol=1e-12)
+
+
 PINS = {
     "assign_ground_truth": pin_assign_ground_truth,
     "assign_copies": pin_assign_copies,
@@ -398,4 +415,5 @@ PINS = {
     "empty_child_far_away": pin_empty_child_far_away,
     "exact_attention": pin_exact_attention,
     "margins": pin_margins,
+    "flat_codebook": pin_flat_codebook,
 }

@@ -67,7 +67,7 @@ def test_assign_validation(L):
     assert _assign(L, dtype=7) == -3
     assert _assign(L, N=-1) == -2
     assert _assign(L, B=-1) == -2
-    assert _assign(L, C=0) == -2
+    assert _assign(L, C=-1) == -2
     assert _assign(L, M0=0) == -2
     assert _assign(L, d=96) == -5
     assert _assign(L, M0=257) == -5
@@ -87,6 +87,7 @@ def test_attention_validation(L):
     mis = ctypes.c_void_p(p.value + 8)
     assert _attn(L, P=-1) == -2
     assert _attn(L, P=5) == -2
+    assert _attn(L, C=0, P=1) == -2  # a flat codebook has no children to refine with
     assert _attn(L, bq=48) == -5
     assert _attn(L, bq=256) == -5
     assert _attn(L, scale=float("nan")) == -2

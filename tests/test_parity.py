@@ -96,6 +96,12 @@ def test_tiled_parents(M0, P):
     _full_check(_data("grid64", M0=M0, H=2, N=2048 + 64 + 5, grid=None), P)
 
 
+@pytest.mark.parametrize("M0", [64, 256])
+def test_flat_codebook(M0):
+    """C = 0: a flat codebook of M0 codewords, plain VQ attention (P = 0)."""
+    _full_check(_data("grid64", M0=M0, C=0, P=0), 0)
+
+
 def test_full_size_grid128():
     """The headline workload at full size: every assignment, count and value
     sum, plus sampled query tiles for importance, top-P and output."""
