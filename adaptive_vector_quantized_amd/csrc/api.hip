@@ -87,7 +87,8 @@ int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, co
       !aligned16(workspace) || (topp && !aligned16(topp)) || (importance && !aligned16(importance)))
     return AVQ_ERR_ALIGN;
   if (workspace_bytes < avq::attention_workspace_bytes(dtype, d, M0, C, (int)BH)) return AVQ_ERR_WORKSPACE;
-  if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
+  if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q, importance != nullptr) > (size_t)kMaxLds)
+    return AVQ_ERR_UNSUPPORTED;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
                                         Y, topp, importance, workspace, (hipStream_t)stream));
 }

@@ -257,7 +257,9 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   }
 }
 
-template <class T, int D, int W>
+// PL: the parents' codewords are held in LDS (M0 <= 64); else they are read
+// from L2 one block ahead of their MFMAs
+template <class T, int D, int W, bool PL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
     const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
@@ -286,18 +288,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int M0p = (M0 + 31) & ~31;
   const int nblkP = M0p / 32;
   const int Pp = P > 0 ? P : 1;
-  const bool parents_lds = M0p <= 64;  // parents' codewords in LDS (else read from L2)
+  constexpr bool parents_lds = PL;
   frag_t* sPC = (frag_t*)smem;                                        // [nblkP*FA] if parents_lds
   pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV]
+  // the children's arrays exist only when P > 0, the importance partials only
+  // when importances are formed
+  const bool need_imp = (P > 0) || (importance != nullptr);
+  const int nCB = P > 0 ? NCB : 0, nCH = P > 0 ? CH : 0;
   frag_t* sCC = (frag_t*)(sPV + nblkP * FV);                          // [NCB*FA]
-  pvfrag_t* sCV = (pvfrag_t*)(sCC + NCB * FA);                        // [NCB*FV]
-  float* sNp = (float*)(sCV + NCB * FV);                              // [M0p] counts
+  pvfrag_t* sCV = (pvfrag_t*)(sCC + nCB * FA);                        // [NCB*FV]
+  float* sNp = (float*)(sCV + nCB * FV);                              // [M0p] counts
   float* sNc = sNp + M0p;                                             // [CH]
-  float* sBp = sNc + CH;                                              // [M0p] 0 or -inf (empty)
+  float* sBp = sNc + nCH;                                             // [M0p] 0 or -inf (empty)
   float* sBc = sBp + M0p;                                             // [CH]
-  float* sNa = sBc + CH;                                              // [M0][W] counts of all children
-  float* sW = sNa + M0 * W;                                           // [nw][M0p]
-  int* sSel = (int*)(sW + nw * M0p);                                  // [nw][Pp]
+  float* sNa = sBc + nCH;                                             // [M0][W] counts of all children
+  float* sW = sNa + (P > 0 ? M0 * W : 0);                             // [nw][M0p]
+  int* sSel = (int*)(sW + (need_imp ? nw * M0p : 0));                 // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [1]
   float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 1) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
 
@@ -331,11 +337,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const pvfrag_t* pvf = (const pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
   const unsigned char* zeros = ws + sig_bytes - kZeroBytes;  // codeword rows past C
   const pvfrag_t* cvf = pvf + nblkP * FV;
-  const bool need_imp = (P > 0) || (importance != nullptr);
   const int nPT = (M0 + 63) / 64;
 
   // ---- once per workgroup: parents into LDS -----------------------------------
-  if (parents_lds) {
+  if constexpr (parents_lds) {
     for (int u = wave; u < nblkP * KS; u += nw) {
       const int b = u / KS, s = u % KS;
       const int j = b * 32 + ql;
@@ -383,7 +388,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     float m = -INFINITY;   // stabiliser of the scaled (log2-domain) logits
     f32x16 lg[2];
 
-    // parents (Alg. 2 lines 2-7), 64 per pass
+    // parents (Alg. 2 lines 2-7), 64 per pass; parents not held in LDS are
+    // read from L2 one 32-row block ahead of their MFMAs
+    frag_t pa[parents_lds ? 1 : KS];
+    auto load_parents = [&](int bb) {
+      if constexpr (!parents_lds) {
+        const int j = bb * 32 + ql;
+        const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) pa[s] = *(const frag_t*)(ap + s * 2 * E);
+      }
+    };
+    if constexpr (!parents_lds) load_parents(0);
     for (int pt = 0; pt < nPT; ++pt) {
       const int j0 = pt * 64;
       const int nblk = min(2, (M0 - j0 + 31) / 32);
@@ -392,14 +408,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         lg[b] = zero16();
         if (b < nblk) {
           const int bb = pt * 2 + b;
-          if (parents_lds) {
+          if constexpr (parents_lds) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
-          } else {
-            const int j = bb * 32 + ql;
-            const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
+          } else if constexpr (!parents_lds) {
+            frag_t cur[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], lg[b]);
+            for (int s = 0; s < KS; ++s) cur[s] = pa[s];
+            if (bb + 1 < nblkP) load_parents(bb + 1);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(cur[s], qf[s], lg[b]);
           }
         }
       }
@@ -704,18 +722,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
 }
 
-size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q) {
+size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance) {
   const size_t es = dtype == 0 ? 4 : 2;   // input and value operand element (same width)
   const size_t M0p = (M0 + 31) & ~31;
   const size_t nw = block_q / 32;
   const size_t CH = d == 64 ? AttnTraits<64>::kChunkRows : AttnTraits<128>::kChunkRows;
   (void)C;
+  const size_t ch = P > 0 ? CH : 0;
   size_t b = (M0p <= 64 ? M0p * d * es : 0);  // parents' codeword fragments
   b += M0p * d * es;                          // parents' value fragments
-  b += 2 * CH * d * es;                       // chunk codeword and value fragments
-  b += 2 * (M0p + CH) * 4;                    // counts and biases
-  b += (size_t)M0 * (C <= 8 ? 8 : 16) * 4;    // counts of all children
-  b += nw * M0p * 4;                          // importance partials
+  b += 2 * ch * d * es;                       // chunk codeword and value fragments
+  b += 2 * (M0p + ch) * 4;                    // counts and biases
+  if (P > 0) b += (size_t)M0 * (C <= 8 ? 8 : 16) * 4;  // counts of all children
+  if (P > 0 || importance) b += nw * M0p * 4;          // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
   b = (b + 15) & ~(size_t)15;
   b += nw * 32 * kYRow * 4;                   // output staging
@@ -740,7 +759,7 @@ int attention_tiles_per_wg(int BH, int N, int bq) {
   return (T + per_bh - 1) / per_bh;
 }
 
-template <class T, int D, int W>
+template <class T, int D, int W, bool PL>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, hipStream_t st) {
@@ -758,8 +777,8 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t smem = attention_smem_bytes(dtype, D, M0, C, P, bq);
-  auto kern = attention_kernel<T, D, W>;
+  const size_t smem = attention_smem_bytes(dtype, D, M0, C, P, bq, importance != nullptr);
+  auto kern = attention_kernel<T, D, W, PL>;
   hipError_t e = raise_lds_limit((const void*)kern, smem);
   if (e != hipSuccess) return e;
   const int tpw = attention_tiles_per_wg(BH, N, bq);
@@ -776,8 +795,13 @@ template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, hipStream_t st) {
-  if (C <= 8) return launch_attn_t<T, D, 8>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
-  return launch_attn_t<T, D, 16>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  const bool pl = M0 <= 64;
+  if (C <= 8) {
+    if (pl) return launch_attn_t<T, D, 8, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+    return launch_attn_t<T, D, 8, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  }
+  if (pl) return launch_attn_t<T, D, 16, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  return launch_attn_t<T, D, 16, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,

@@ -13,7 +13,7 @@ namespace avq {
 hipError_t raise_lds_limit(const void* kernel, size_t bytes);
 
 size_t assign_smem_bytes(int dtype, int d, int M0, int C);
-size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q);
+size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance);
 
 // Children rows staged in LDS per chunk by the attention kernel.
 template <int D>
