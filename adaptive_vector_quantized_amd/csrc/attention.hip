@@ -38,6 +38,7 @@
 // Children of a selected parent occupy W (8 or 16) consecutive accumulator
 // registers of one lane half, so S = 32 / W parents share a 32-row block.
 #include <algorithm>
+#include <cfloat>
 
 #include "avq_device.h"
 #include "avq_launch.h"
@@ -151,7 +152,7 @@ constexpr int kYRow = 68;  // floats per staged output row (64 dims + 4 to sprea
 
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   const size_t pes = dtype == 0 ? 4 : 2;
-  const size_t M0p = (M0 + 31) & ~31;
+  const size_t M0p = attn_parent_rows(M0);
   const size_t W = C <= 8 ? 8 : 16;
   const size_t per = align256((M0p * d + (size_t)M0 * W * d) * pes);
   return align256((size_t)BH * 4) + kZeroBytes + (size_t)BH * per;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Mt = M0 * (1 + C);
-  const int M0p = (M0 + 31) & ~31;
+  const int M0p = attn_parent_rows(M0);
   const float* vs = vsum + (int64_t)bh * Mt * D;
   const int nP = (M0p / 32) * KV * 2 * D;  // parent fragments
   const int nF = nP + M0 * (W / E) * D;    // + child fragments
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int nthreads = blockDim.x;
   const int nw = nthreads >> 6;
   const int Mt = M0 * (1 + C);
-  const int M0p = (M0 + 31) & ~31;
+  const int M0p = attn_parent_rows(M0);
   const int nblkP = M0p / 32;
   const int Pp = P > 0 ? P : 1;
   constexpr bool parents_lds = PL;
@@ -384,12 +385,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     f32x16 xacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) xacc[db] = zero16();
-    float zp = 0.0f;       // denominator over this lane half's codewords
-    float m = -INFINITY;   // stabiliser of the scaled (log2-domain) logits
+    float zp = 0.0f;  // denominator over this lane half's codewords
+    // stabiliser of the scaled (log2-domain) logits; finite from the start so
+    // that an all-empty pass (logits -inf) gives weights exp2(-inf) = 0 and the
+    // first real maximum rescales the (zero) accumulators by exp2(-huge) = 0
+    float m = -FLT_MAX;
     f32x16 lg[2];
 
-    // parents (Alg. 2 lines 2-7), 64 per pass; parents not held in LDS are
-    // read from L2 one 32-row block ahead of their MFMAs
+    // parents (Alg. 2 lines 2-7), 64 per pass (the padding rows past M0 have
+    // count 0 and logit -inf); parents not held in LDS are read from L2 one
+    // 32-row block ahead of their MFMAs
     frag_t pa[parents_lds ? 1 : KS];
     auto load_parents = [&](int bb) {
       if constexpr (!parents_lds) {
@@ -402,86 +407,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if constexpr (!parents_lds) load_parents(0);
     for (int pt = 0; pt < nPT; ++pt) {
       const int j0 = pt * 64;
-      const int nblk = min(2, (M0 - j0 + 31) / 32);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
+        const int bb = pt * 2 + b;
         lg[b] = zero16();
-        if (b < nblk) {
-          const int bb = pt * 2 + b;
-          if constexpr (parents_lds) {
+        if constexpr (parents_lds) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
-          } else if constexpr (!parents_lds) {
-            frag_t cur[KS];
+          for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
+        } else {
+          frag_t cur[KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) cur[s] = pa[s];
-            if (bb + 1 < nblkP) load_parents(bb + 1);
+          for (int s = 0; s < KS; ++s) cur[s] = pa[s];
+          if (bb + 1 < nblkP) load_parents(bb + 1);
 #pragma unroll
-            for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(cur[s], qf[s], lg[b]);
+          for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(cur[s], qf[s], lg[b]);
+        }
+      }
+      if (!all_parents || j0 + 64 > M0) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const f32x4* bp = (const f32x4*)(sBp + j0 + b * 32 + 8 * hh);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) lg[b][q * 4 + u] += b4[u];
           }
         }
       }
       float tm = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (b < nblk) {
-          if (!all_parents || j0 + 32 * (b + 1) > M0) {
-            const f32x4* bp = (const f32x4*)(sBp + j0 + b * 32 + 8 * hh);
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
-#pragma unroll
-              for (int u = 0; u < 4; ++u) lg[b][q * 4 + u] += b4[u];
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tm = fmaxf(tm, lg[b][r]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) lg[b][r] = -INFINITY;
-        }
-      }
+        for (int r = 0; r < 16; ++r) tm = fmaxf(tm, lg[b][r]);
       tm = xhalf_max(tm) * sl2;
-      if (tm > m + kLazy || m == -INFINITY) {
-        const float mn = fmaxf(m, tm);
-        if (mn != -INFINITY) {
-          const float f = fast_exp2(m - mn);
-          zp *= f;
+      if (tm > m + kLazy) {
+        const float f = fast_exp2(m - tm);
+        zp *= f;
 #pragma unroll
-          for (int db = 0; db < DB; ++db) xacc[db] *= f;
-          m = mn;
-        }
+        for (int db = 0; db < DB; ++db) xacc[db] *= f;
+        m = tm;
       }
-      if (m != -INFINITY) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          if (b < nblk) {
-            const f32x4* np4 = (const f32x4*)(sNp + j0 + b * 32 + 8 * hh);
+      for (int b = 0; b < 2; ++b) {
+        const f32x4* np4 = (const f32x4*)(sNp + j0 + b * 32 + 8 * hh);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 n4 = np4[(q >> 1) * 4 + (q & 1)];
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 n4 = np4[(q >> 1) * 4 + (q & 1)];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) {
-                const float a = fast_exp2(fmaf(lg[b][q * 4 + u], sl2, -m));
-                lg[b][q * 4 + u] = a;
-                zp = fmaf(a, n4[u], zp);
-              }
-            }
-            const int bb = pt * 2 + b;
-#pragma unroll
-            for (int k = 0; k < KV; ++k) {
-              const pvfrag_t bf = pv_operand<T, KV>(lg[b], k);
-#pragma unroll
-              for (int db = 0; db < DB; ++db)
-                xacc[db] = T::mma_pv(sPV[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
-            }
-          } else {
-            lg[b] = zero16();
+          for (int u = 0; u < 4; ++u) {
+            const float a = fast_exp2(fmaf(lg[b][q * 4 + u], sl2, -m));
+            lg[b][q * 4 + u] = a;
+            zp = fmaf(a, n4[u], zp);
           }
         }
-      } else {
-        lg[0] = zero16();
-        lg[1] = zero16();
+        const int bb = pt * 2 + b;
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+          const pvfrag_t bf = pv_operand<T, KV>(lg[b], k);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            xacc[db] = T::mma_pv(sPV[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
+        }
       }
     }
 
@@ -490,7 +477,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       const float rz = qv ? 1.0f / xhalf_sum(zp) : 0.0f;
       for (int pt = 0; pt < nPT; ++pt) {
         const int j0 = pt * 64;
-        const int nblk = min(2, (M0 - j0 + 31) / 32);
         float t[32];
         if (nPT == 1) {
 #pragma unroll
@@ -508,28 +494,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             f32x16 l2 = zero16();
-            if (b < nblk) {
-              const int j = j0 + 32 * b + ql;
-              const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
+            const int j = j0 + 32 * b + ql;
+            const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
 #pragma unroll
-              for (int s = 0; s < KS; ++s) l2 = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], l2);
-            }
+            for (int s = 0; s < KS; ++s) l2 = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], l2);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float n = b < nblk ? sNp[j0 + b * 32 + col_of(r, hh)] : 0.0f;
+              const float n = sNp[j0 + b * 32 + col_of(r, hh)];
               t[b * 16 + r] = n > 0.0f ? fast_exp2(fmaf(l2[r], sl2, -m)) * n * rz : 0.0f;
             }
           }
         }
-        if (nblk == 2) {
-          rs_half32(t, lane);
-          const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
-          if (j < M0) sW[wave * M0p + j] = t[0];
-        } else {
-          rs_half16(t, lane);
-          const int j = j0 + row_of(ql & 15, hh);
-          if (ql < 16 && j < M0) sW[wave * M0p + j] = t[0];
-        }
+        rs_half32(t, lane);
+        const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
+        if (j < M0) sW[wave * M0p + j] = t[0];
       }
       __syncthreads();
       // every wave forms the totals and its own copy of the selection
@@ -724,7 +702,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
 size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance) {
   const size_t es = dtype == 0 ? 4 : 2;   // input and value operand element (same width)
-  const size_t M0p = (M0 + 31) & ~31;
+  const size_t M0p = attn_parent_rows(M0);
   const size_t nw = block_q / 32;
   const size_t CH = d == 64 ? AttnTraits<64>::kChunkRows : AttnTraits<128>::kChunkRows;
   (void)C;
@@ -768,7 +746,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
   {
     constexpr int E = T::E, KV = 16 / E;
-    const int M0p = (M0 + 31) & ~31;
+    const int M0p = attn_parent_rows(M0);
     const int nF = (M0p / 32) * KV * 2 * D + M0 * (W / E) * D;
     const int per_part = kPrepThreads * kPrepFrag;
     const int parts = std::max(8, (nF + per_part - 1) / per_part);

@@ -15,6 +15,10 @@ hipError_t raise_lds_limit(const void* kernel, size_t bytes);
 size_t assign_smem_bytes(int dtype, int d, int M0, int C);
 size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance);
 
+// Parent rows of the attention kernel's operands: M0 padded to whole 64-row
+// passes (padding rows carry zero values and count 0).
+__host__ __device__ constexpr int attn_parent_rows(int M0) { return (M0 + 63) & ~63; }
+
 // Children rows staged in LDS per chunk by the attention kernel.
 template <int D>
 struct AttnTraits {
