@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sNa = sBc + nCH;                                             // [M0][W] counts of all children
   float* sW = sNa + (P > 0 ? M0 * W : 0);                             // [nw][M0p]
   int* sSel = (int*)(sW + (need_imp ? nw * M0p : 0));                 // [nw][Pp]
-  int* sFlag = sSel + nw * Pp;                                        // [1]
-  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 1) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
+  int* sFlag = sSel + nw * Pp;                                        // [2] all parents hold keys; chunk needs masks
+  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 2) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -554,15 +554,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     // children of the selected parents (Alg. 2 lines 10-19), CH rows per chunk
     if (P > 0) {
       const int* sel = sSel + wave * Pp;
-      const float invC = 1.0f / (float)C;
+      const float sl2C = sl2 / (float)C;  // Eq. 8's mean folded into the logit scale
       for (int cs = 0; cs < P; cs += NCB * S) {
-        const int nbk = min(NCB, (P - cs + S - 1) / S);
         if (cs > 0) __syncthreads();  // readers of the previous chunk are done
-        // codeword fragments: one DMA per (block, k-step); lane = (row, half)
+        // codeword fragments: one DMA per (block, k-step); lane = (row, half).
+        // Slots past P and rows past C read zeros.
         {
           const int r = r_of_row(ql), hr = h_of_row(ql);
           const int s_row = 2 * (r / W) + hr, c_row = r % W;
-          for (int u = wave; u < nbk * KS; u += nw) {
+          for (int u = wave; u < NCB * KS; u += nw) {
             const int b = u / KS, s = u % KS;
             const int gs = cs + b * S + s_row;
             const bool ok = gs < P && c_row < C;
@@ -571,7 +571,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           }
         }
         // value fragments: one DMA per (block, k-step, half, 64 dims); lane = dim
-        for (int u = wave; u < nbk * KV * 2 * (D / 64); u += nw) {
+        for (int u = wave; u < NCB * KV * 2 * (D / 64); u += nw) {
           const int dc = u % (D / 64), t = u / (D / 64);
           const int h2 = t % 2, bk = t / 2, k = bk % KV, b = bk / KV;
           const int r = k * E;
@@ -579,42 +579,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const int p = gs < P ? sel[gs] : sel[0];
           lds_dma<BV>(cvf + ((int64_t)p * (W / E) + gg) * D + dc * 64 + lane, sCV + ((b * KV + k) * 2 + h2) * D + dc * 64);
         }
-        for (int c = tid; c < nbk * 32; c += nthreads) {
-          const int b = c >> 5, qq = c & 31;
+        // counts and biases of the chunk's NCB * 32 = 64 rows (one per lane of
+        // wave 0), and whether any row is empty (then the chunk takes masks)
+        static_assert(NCB * 32 == 64, "one chunk row per lane of wave 0");
+        if (wave == 0) {
+          const int b = lane >> 5, qq = lane & 31;
           const int r = r_of_col(qq), hc = h_of_col(qq);
           const int gs = cs + b * S + 2 * (r / W) + hc, cc = r % W;
           const float n = gs < P ? sNa[sel[gs] * W + cc] : 0.0f;
-          sNc[c] = n;
-          sBc[c] = n > 0.0f ? 0.0f : -INFINITY;
+          sNc[lane] = n;
+          sBc[lane] = n > 0.0f ? 0.0f : -INFINITY;
+          const bool any_empty = __builtin_amdgcn_ballot_w64(!(n > 0.0f)) != 0;
+          if (lane == 0) sFlag[1] = any_empty ? 1 : 0;
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (cs == 0) prefetch_next();
+        const bool chunk_masked = __builtin_amdgcn_readfirstlane(sFlag[1]) != 0;
 
-        // logits of the whole chunk, masked (empty children -> -inf), one max
+        // logits of the whole chunk
         f32x16 cl[NCB];
 #pragma unroll
         for (int b = 0; b < NCB; ++b) {
           cl[b] = zero16();
-          if (b < nbk) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) cl[b] = T::mma_in(sCC[(b * KS + s) * 64 + lane], qf[s], cl[b]);
-          }
+          for (int s = 0; s < KS; ++s) cl[b] = T::mma_in(sCC[(b * KS + s) * 64 + lane], qf[s], cl[b]);
         }
-        // stabiliser over the non-empty children (a -inf bias masks the rest);
-        // the logits themselves stay unmasked for Eq. 8
-        float tm = -INFINITY;
+        // Eq. 8: the parent logit is the mean of its C child logits, taken
+        // before any masking; the W - C padding rows have zero codewords and
+        // add nothing
+        float sp[NCB][16 / W];
 #pragma unroll
         for (int b = 0; b < NCB; ++b)
-          if (b < nbk) {
+#pragma unroll
+          for (int g2 = 0; g2 < 16 / W; ++g2) {
+            float acc = cl[b][g2 * W];
+#pragma unroll
+            for (int c = 1; c < W; ++c) acc += cl[b][g2 * W + c];
+            sp[b][g2] = acc;
+          }
+        // children without keys, padding rows and slots past P: logit -inf
+        // (weight exactly 0); a chunk without such rows skips the masks
+        if (chunk_masked) {
+#pragma unroll
+          for (int b = 0; b < NCB; ++b) {
             const f32x4* bc = (const f32x4*)(sBc + b * 32 + 8 * hh);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const f32x4 b4 = bc[(q >> 1) * 4 + (q & 1)];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) tm = fmaxf(tm, cl[b][q * 4 + u] + b4[u]);
+              for (int u = 0; u < 4; ++u) cl[b][q * 4 + u] += b4[u];
             }
           }
+        }
+        float tm = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NCB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tm = fmaxf(tm, cl[b][r]);
         tm = xhalf_max(tm) * sl2;
         if (tm > m + kLazy) {
           const float f = fast_exp2(m - tm);
@@ -625,41 +647,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
 #pragma unroll
         for (int b = 0; b < NCB; ++b) {
-          if (b < nbk) {
-            const f32x4* nc = (const f32x4*)(sNc + b * 32 + 8 * hh);
-            const f32x4* bc = (const f32x4*)(sBc + b * 32 + 8 * hh);
+          const f32x4* nc = (const f32x4*)(sNc + b * 32 + 8 * hh);
 #pragma unroll
-            for (int g2 = 0; g2 < 16 / W; ++g2) {
-              // Eq. 8: the parent logit is the mean of its C child logits; the
-              // W - C padding rows have zero codewords and add nothing.  A slot
-              // beyond P contributes nothing; an empty selected parent gets a
-              // bounded weight (its children carry zero values and counts).
-              float sp = cl[b][g2 * W];
+          for (int g2 = 0; g2 < 16 / W; ++g2) {
+            // a slot beyond P contributes nothing; an empty selected parent
+            // gets a bounded weight (its children carry zero values and counts)
+            const bool slot_ok = cs + b * S + 2 * g2 + hh < P;
+            const float ap = slot_ok ? fast_exp2(fminf(fmaf(sp[b][g2], sl2C, -m), kLazy + 1.0f)) : 0.0f;
 #pragma unroll
-              for (int c = 1; c < W; ++c) sp += cl[b][g2 * W + c];
-              const bool slot_ok = cs + b * S + 2 * g2 + hh < P;
-              const float ap = slot_ok ? fast_exp2(fminf(fmaf(sp * invC, sl2, -m), kLazy + 1.0f)) : 0.0f;
+            for (int q = (g2 * W) / 4; q < (g2 * W + W) / 4; ++q) {
+              const f32x4 n4 = nc[(q >> 1) * 4 + (q & 1)];
 #pragma unroll
-              for (int q = (g2 * W) / 4; q < (g2 * W + W) / 4; ++q) {
-                const f32x4 n4 = nc[(q >> 1) * 4 + (q & 1)];
-                const f32x4 b4 = bc[(q >> 1) * 4 + (q & 1)];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                  // empty and padding children: weight 0 - ap against zero
-                  // values and counts, so they add exactly nothing
-                  const float da = fast_exp2(fmaf(cl[b][q * 4 + u] + b4[u], sl2, -m)) - ap;
-                  cl[b][q * 4 + u] = da;
-                  zp = fmaf(da, n4[u], zp);
-                }
+              for (int u = 0; u < 4; ++u) {
+                // empty and padding children: weight 0 - ap against zero
+                // values and counts, so they add exactly nothing
+                const float da = fast_exp2(fmaf(cl[b][q * 4 + u], sl2, -m)) - ap;
+                cl[b][q * 4 + u] = da;
+                zp = fmaf(da, n4[u], zp);
               }
             }
+          }
 #pragma unroll
-            for (int k = 0; k < KV; ++k) {
-              const pvfrag_t bf = pv_operand<T, KV>(cl[b], k);
+          for (int k = 0; k < KV; ++k) {
+            const pvfrag_t bf = pv_operand<T, KV>(cl[b], k);
 #pragma unroll
-              for (int db = 0; db < DB; ++db)
-                xacc[db] = T::mma_pv(sCV[((b * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
-            }
+            for (int db = 0; db < DB; ++db)
+              xacc[db] = T::mma_pv(sCV[((b * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
           }
         }
       }
