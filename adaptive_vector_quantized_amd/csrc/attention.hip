@@ -377,6 +377,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   __syncthreads();
   const bool all_parents = sFlag[0] != 0;
 
+  // Output staging: a wave's 32 rows x 64 dims in LDS, written out by
+  // store_rows with four whole rows per store instruction.  At d = 64 a tile's
+  // rows stay staged until the next tile's children have landed in LDS (or,
+  // without children, until its parent pass is done): a wait for staged
+  // children counts every earlier memory operation, stores included, so the
+  // stores are issued after that wait and overlap the next computation.
+  constexpr bool kDeferY = (D == 64);
+  float* yw = sY + wave * 32 * kYRow;
+  int y_pending = -1;  // first query of the rows staged and not yet stored, or -1
+  auto store_rows = [&](int q0, int half) {
+    __builtin_amdgcn_wave_barrier();
+    const int r0 = lane >> 4, c4 = (lane & 15) * 4;
+    const float* src = yw + r0 * kYRow + c4;
+    float* dst = Yb + (int64_t)(q0 + r0) * D + half * 64 + c4;
+    if (q0 + 32 <= N) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (q0 + r0 + 4 * k < N) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
+    }
+    y_pending = -1;
+  };
+
   // ---- query tiles ------------------------------------------------------------
   for (int tile = tile0; tile < tile1; ++tile) {
     const int qi = tile * bq + wave * 32 + ql;
@@ -549,7 +574,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
     };
-    if (P == 0) prefetch_next();
+    if (P == 0) {
+      prefetch_next();
+      if (kDeferY && y_pending >= 0) store_rows(y_pending, 0);
+    }
 
     // children of the selected parents (Alg. 2 lines 10-19), CH rows per chunk
     if (P > 0) {
@@ -595,6 +623,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (cs == 0) prefetch_next();
+        if (kDeferY && cs + NCB * S >= P && y_pending >= 0) store_rows(y_pending, 0);
         const bool chunk_masked = __builtin_amdgcn_readfirstlane(sFlag[1]) != 0;
 
         // logits of the whole chunk
@@ -679,11 +708,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
 
     // Y = x / z (Alg. 2 line 20).  A lane holds 4-float runs of its query's
-    // row; the wave's 32 x 64 block goes through LDS so that every store
-    // instruction writes four whole rows (64 dims at a time).
+    // row; the wave's output goes through LDS 64 dims at a time so that every
+    // store instruction writes four whole rows.  At d = 64 the stores of a
+    // tile are issued during the next tile (see store_rows).
     const float zt = xhalf_sum(zp);
     const float f = qv ? sig / zt : 0.0f;
-    float* yw = sY + wave * 32 * kYRow;
+    const int q0 = tile * bq + wave * 32;
+    if (kDeferY && y_pending >= 0) store_rows(y_pending, 0);  // not reached: every tile flushes
 #pragma unroll
     for (int half = 0; half < DB / 2; ++half) {
       __builtin_amdgcn_wave_barrier();
@@ -696,21 +727,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           *(f32x4*)(yw + ql * kYRow + dbl * 32 + 8 * i + 4 * hh) = o;
         }
       __builtin_amdgcn_wave_barrier();
-      const int q0 = tile * bq + wave * 32, r0 = lane >> 4, c4 = (lane & 15) * 4;
-      const float* src = yw + r0 * kYRow + c4;
-      float* dst = Yb + (int64_t)(q0 + r0) * D + half * 64 + c4;
-      if (q0 + 32 <= N) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (q0 + r0 + 4 * k < N) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
-      }
+      if constexpr (kDeferY)
+        y_pending = q0;
+      else
+        store_rows(q0, half);
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qn[s];
   }
+  if (kDeferY && y_pending >= 0) store_rows(y_pending, 0);
 }
 
 size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance) {
