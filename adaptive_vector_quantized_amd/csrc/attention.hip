@@ -378,7 +378,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const bool all_parents = sFlag[0] != 0;
 
   // Output staging: a wave's 32 rows x 64 dims in LDS, written out by
-  // store_rows with four whole rows per store instruction.  At d = 64 a tile's
+  // store_rows with four whole rows per store instruction, as streaming
+  // (non-temporal) stores: the output is never read back here, and keeping
+  // it out of L2 leaves L2 to the codewords and value fragments.  At d = 64 a tile's
   // rows stay staged until the next tile's children have landed in LDS (or,
   // without children, until its parent pass is done): a wait for staged
   // children counts every earlier memory operation, stores included, so the
@@ -393,11 +395,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     float* dst = Yb + (int64_t)(q0 + r0) * D + half * 64 + c4;
     if (q0 + 32 <= N) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
+      for (int k = 0; k < 8; ++k) __builtin_nontemporal_store(*(const f32x4*)(src + 4 * k * kYRow), (f32x4*)(dst + 4 * k * D));
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (q0 + r0 + 4 * k < N) *(f32x4*)(dst + 4 * k * D) = *(const f32x4*)(src + 4 * k * kYRow);
+        if (q0 + r0 + 4 * k < N)
+          __builtin_nontemporal_store(*(const f32x4*)(src + 4 * k * kYRow), (f32x4*)(dst + 4 * k * D));
     }
     y_pending = -1;
   };
