@@ -48,15 +48,17 @@ struct RawV<TF32, 4> { using t = f32x4; };
 
 // Raw buffer load (bounds-checked by the descriptor: reads past num_records
 // return zero).  Word 3 of the descriptor is the gfx9-family raw-access value.
-// voff: per-lane byte offset, soff: wave-uniform byte offset.
+// voff: per-lane byte offset, soff: wave-uniform byte offset.  The values are
+// read exactly once, so the load is a streaming (non-temporal) one.
+constexpr int kNonTemporal = 2;  // cache-policy bit of the buffer load
 template <class R>
 __device__ __forceinline__ R buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   if constexpr (sizeof(R) == 4)
-    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal));
   else if constexpr (sizeof(R) == 8)
-    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal));
   else
-    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return __builtin_bit_cast(R, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal));
 }
 constexpr int kBufWord3 = 0x00020000;
 

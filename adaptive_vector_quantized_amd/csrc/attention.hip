@@ -148,7 +148,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&u)[NG], int M0, int 
 // A fragment is E consecutive operand elements (8 fp16, or 1 fp32).
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kZeroBytes = 256;
-constexpr int kYRow = 68;  // floats per staged output row (64 dims + 4 to spread LDS banks)
+constexpr int kYRow = 36;  // floats per staged output row (32 dims + 4 to spread LDS banks)
 
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   const size_t pes = dtype == 0 ? 4 : 2;
@@ -302,8 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sNc = sNp + M0p;                                             // [CH]
   float* sBp = sNc + nCH;                                             // [M0p] 0 or -inf (empty)
   float* sBc = sBp + M0p;                                             // [CH]
-  float* sNa = sBc + nCH;                                             // [M0][W] counts of all children
-  float* sW = sNa + (P > 0 ? M0 * W : 0);                             // [nw][M0p]
+  float* sW = sBc + nCH;                                              // [nw][M0p]
   int* sSel = (int*)(sW + (need_imp ? nw * M0p : 0));                 // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [2] all parents hold keys; chunk needs masks
   float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 2) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
@@ -358,14 +357,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     sBp[c] = n > 0.0f ? 0.0f : -INFINITY;
     if (j < M0 && !(n > 0.0f)) sFlag[0] = 0;
   }
-  // counts of every child, slot-padded to W (the per-chunk staging then
-  // reads LDS, not global memory)
-  if (P > 0) {
-    for (int i = tid; i < M0 * W; i += nthreads) {
-      const int p = i / W, c = i % W;
-      sNa[i] = c < C ? (float)nb[M0 + p * C + c] : 0.0f;
-    }
-  }
   frag_t qf[KS];
   {
     const int qi = tile0 * bq + wave * 32 + ql;
@@ -377,32 +368,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   __syncthreads();
   const bool all_parents = sFlag[0] != 0;
 
-  // Output staging: a wave's 32 rows x 64 dims in LDS, written out by
-  // store_rows with four whole rows per store instruction, as streaming
-  // (non-temporal) stores: the output is never read back here, and keeping
-  // it out of L2 leaves L2 to the codewords and value fragments.  At d = 64 a tile's
-  // rows stay staged until the next tile's children have landed in LDS (or,
-  // without children, until its parent pass is done): a wait for staged
-  // children counts every earlier memory operation, stores included, so the
-  // stores are issued after that wait and overlap the next computation.
-  constexpr bool kDeferY = (D == 64);
+  // Output staging: a wave's 32 rows x 32 dims in LDS, written out by
+  // store_rows with eight whole 128-byte row segments per store instruction,
+  // as streaming (non-temporal) stores: the output is never read back here,
+  // and keeping it out of L2 leaves L2 to the codewords and value fragments.
   float* yw = sY + wave * 32 * kYRow;
-  int y_pending = -1;  // first query of the rows staged and not yet stored, or -1
-  auto store_rows = [&](int q0, int half) {
+  auto store_rows = [&](int q0, int db) {
     __builtin_amdgcn_wave_barrier();
-    const int r0 = lane >> 4, c4 = (lane & 15) * 4;
+    const int r0 = lane >> 3, c4 = (lane & 7) * 4;
     const float* src = yw + r0 * kYRow + c4;
-    float* dst = Yb + (int64_t)(q0 + r0) * D + half * 64 + c4;
+    float* dst = Yb + (int64_t)(q0 + r0) * D + db * 32 + c4;
     if (q0 + 32 <= N) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) __builtin_nontemporal_store(*(const f32x4*)(src + 4 * k * kYRow), (f32x4*)(dst + 4 * k * D));
+      for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(*(const f32x4*)(src + 8 * k * kYRow), (f32x4*)(dst + 8 * k * D));
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (q0 + r0 + 4 * k < N)
-          __builtin_nontemporal_store(*(const f32x4*)(src + 4 * k * kYRow), (f32x4*)(dst + 4 * k * D));
+      for (int k = 0; k < 4; ++k)
+        if (q0 + r0 + 8 * k < N)
+          __builtin_nontemporal_store(*(const f32x4*)(src + 8 * k * kYRow), (f32x4*)(dst + 8 * k * D));
     }
-    y_pending = -1;
   };
 
   // ---- query tiles ------------------------------------------------------------
@@ -506,7 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int pt = 0; pt < nPT; ++pt) {
         const int j0 = pt * 64;
         float t[32];
-        if (nPT == 1) {
+        if (parents_lds || nPT == 1) {  // one pass: its weights are still in registers
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const f32x4* np4 = (const f32x4*)(sNp + b * 32 + 8 * hh);
@@ -555,7 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
       if (P > 0) {
         int* gout = (topp && wave == 0) ? topp + ((int64_t)bh * ntiles + tile) * P : nullptr;
-        if (M0 <= 64) {
+        if (parents_lds || M0 <= 64) {
           uint32_t u1[1] = {u[0]};
           select_top<1>(u1, M0, P, lane, sSel + wave * Pp, gout);
         } else if (M0 <= 128) {
@@ -577,10 +561,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
       for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
     };
-    if (P == 0) {
-      prefetch_next();
-      if (kDeferY && y_pending >= 0) store_rows(y_pending, 0);
-    }
+    if (P == 0) prefetch_next();
 
     // children of the selected parents (Alg. 2 lines 10-19), CH rows per chunk
     if (P > 0) {
@@ -617,7 +598,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const int b = lane >> 5, qq = lane & 31;
           const int r = r_of_col(qq), hc = h_of_col(qq);
           const int gs = cs + b * S + 2 * (r / W) + hc, cc = r % W;
-          const float n = gs < P ? sNa[sel[gs] * W + cc] : 0.0f;
+          const float n = (gs < P && cc < C) ? (float)nb[M0 + sel[gs] * C + cc] : 0.0f;
           sNc[lane] = n;
           sBc[lane] = n > 0.0f ? 0.0f : -INFINITY;
           const bool any_empty = __builtin_amdgcn_ballot_w64(!(n > 0.0f)) != 0;
@@ -626,7 +607,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (cs == 0) prefetch_next();
-        if (kDeferY && cs + NCB * S >= P && y_pending >= 0) store_rows(y_pending, 0);
         const bool chunk_masked = __builtin_amdgcn_readfirstlane(sFlag[1]) != 0;
 
         // logits of the whole chunk
@@ -649,6 +629,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
             for (int c = 1; c < W; ++c) acc += cl[b][g2 * W + c];
             sp[b][g2] = acc;
+            // formed here, before the masks, so that the unmasked logits are
+            // dead once they are masked in place
+            asm volatile("" : "+v"(sp[b][g2]));
           }
         // children without keys, padding rows and slots past P: logit -inf
         // (weight exactly 0); a chunk without such rows skips the masks
@@ -711,34 +694,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
 
     // Y = x / z (Alg. 2 line 20).  A lane holds 4-float runs of its query's
-    // row; the wave's output goes through LDS 64 dims at a time so that every
-    // store instruction writes four whole rows.  At d = 64 the stores of a
-    // tile are issued during the next tile (see store_rows).
+    // row; the wave's output goes through LDS 32 dims at a time.
     const float zt = xhalf_sum(zp);
     const float f = qv ? sig / zt : 0.0f;
     const int q0 = tile * bq + wave * 32;
-    if (kDeferY && y_pending >= 0) store_rows(y_pending, 0);  // not reached: every tile flushes
 #pragma unroll
-    for (int half = 0; half < DB / 2; ++half) {
+    for (int db = 0; db < DB; ++db) {
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int dbl = 0; dbl < 2; ++dbl)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x16& a = xacc[2 * half + dbl];
-          const f32x4 o = {a[4 * i] * f, a[4 * i + 1] * f, a[4 * i + 2] * f, a[4 * i + 3] * f};
-          *(f32x4*)(yw + ql * kYRow + dbl * 32 + 8 * i + 4 * hh) = o;
-        }
-      __builtin_amdgcn_wave_barrier();
-      if constexpr (kDeferY)
-        y_pending = q0;
-      else
-        store_rows(q0, half);
+      for (int i = 0; i < 4; ++i) {
+        const f32x16& a = xacc[db];
+        const f32x4 o = {a[4 * i] * f, a[4 * i + 1] * f, a[4 * i + 2] * f, a[4 * i + 3] * f};
+        *(f32x4*)(yw + ql * kYRow + 8 * i + 4 * hh) = o;
+      }
+      store_rows(q0, db);
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qn[s];
   }
-  if (kDeferY && y_pending >= 0) store_rows(y_pending, 0);
 }
 
 size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance) {
@@ -752,7 +725,6 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   b += M0p * d * es;                          // parents' value fragments
   b += 2 * ch * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
-  if (P > 0) b += (size_t)M0 * (C <= 8 ? 8 : 16) * 4;  // counts of all children
   if (P > 0 || importance) b += nw * M0p * 4;          // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
   b = (b + 15) & ~(size_t)15;
