@@ -101,19 +101,21 @@ __device__ __forceinline__ void lds_dma(const void* gptr, void* lds_base) {
 
 // Top-P of Alg. 2 over the importances one wave holds (parent j = 64 g + lane
 // in u[g]; non-negative floats as bit patterns, so integer order is value
-// order).  A radix search on the bits finds the P-th largest value thr; the
-// chosen set is everything above thr plus the lowest-index parents equal to
-// it (the tie rule of the oracle), written ascending to out[0..P).
+// order).  A radix search on the bits, from the top, raises a threshold thr
+// while at least P values reach it; it stops early once exactly P do (they
+// are then the answer), else it ends at the P-th largest value.  The chosen
+// set is everything above thr plus the lowest-index parents equal to it (the
+// tie rule of the oracle), written ascending to out[0..P).
 template <int NG>
 __device__ __forceinline__ void select_top(const uint32_t (&u)[NG], int M0, int P, int lane, int* out, int* gout) {
   uint32_t thr = 0;
-#pragma unroll 2
   for (int bit = 30; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
     int cnt = 0;
 #pragma unroll
     for (int g = 0; g < NG; ++g) cnt += __popcll(__ballot(u[g] >= cand));
     thr = cnt >= P ? cand : thr;
+    if (cnt == P) break;
   }
   int above = 0;
 #pragma unroll
@@ -490,17 +492,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int pt = 0; pt < nPT; ++pt) {
         const int j0 = pt * 64;
         float t[32];
-        if (parents_lds || nPT == 1) {  // one pass: its weights are still in registers
+        if constexpr (parents_lds) {  // one pass (M0 <= 64): its weights are still in registers
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const f32x4* np4 = (const f32x4*)(sNp + b * 32 + 8 * hh);
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 n4 = np4[(q >> 1) * 4 + (q & 1)];
-#pragma unroll
-              for (int u = 0; u < 4; ++u) t[b * 16 + q * 4 + u] = lg[b][q * 4 + u] * (n4[u] * rz);
-            }
-          }
+            for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * rz;
         } else {
           // second pass with the final stabiliser and denominator (exact Z of Eq. 7)
 #pragma unroll
@@ -517,9 +513,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             }
           }
         }
+        // one pass: the count n_j of Eq. 7 is a factor of the whole sum over
+        // the tile's queries, applied once after the reduction (the second
+        // pass has it in every term)
         rs_half32(t, lane);
         const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
-        if (j < M0) sW[wave * M0p + j] = t[0];
+        const float nj = parents_lds ? sNp[32 * (ql >> 4) + col_of(ql & 15, hh)] : 1.0f;
+        if (j < M0) sW[wave * M0p + j] = t[0] * nj;
       }
       __syncthreads();
       // every wave forms the totals and its own copy of the selection
