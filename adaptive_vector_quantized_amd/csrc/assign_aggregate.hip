@@ -328,11 +328,10 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   }
 
   // ---- values of this wave's keys into registers ------------------------
-  // Half hh of the wave owns the KH consecutive keys from seg0; lane ql of
-  // the half holds dims EPL*ql .. EPL*ql+EPL-1 of every one of them.  Keys
+  // Half hh of the wave owns the KH consecutive keys from wave * KPW + hh *
+  // KH; lane ql of the half holds dims EPL*ql .. EPL*ql+EPL-1 of every one of them.  Keys
   // past the end of the sequence read as zero (descriptor bound).
   constexpr int KH = KPW / 2;
-  const int seg0 = wave * KPW + hh * KH;
   raw_t vr[KH];
   {
     const int w0 = __builtin_amdgcn_readfirstlane(wave * KPW);

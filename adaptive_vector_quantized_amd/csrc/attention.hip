@@ -90,6 +90,19 @@ __device__ __forceinline__ int parent_of_col(int c) {
 
 // asynchronous copy of BYTES per lane from global memory into LDS at
 // lds_base + lane * BYTES (lds_base must be the same for the whole wave)
+// The same through a buffer descriptor (base and size in scalar registers,
+// a 32-bit byte offset per lane): a fragment at or past the descriptor's size
+// reads as zeros.
+constexpr int kBufWord3 = 0x00020000;     // word 3 of a raw gfx9-family descriptor
+constexpr int kOutOfRange = 0x7FFFFFF0;   // a byte offset past any descriptor here
+template <int BYTES>
+__device__ __forceinline__ void lds_dma_buf(__amdgpu_buffer_rsrc_t rs, int voff, void* lds_base) {
+  static_assert(BYTES == 16 || BYTES == 4, "fragment size");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 4, voff, 0, 0, 0);
+}
 template <int BYTES>
 __device__ __forceinline__ void lds_dma(const void* gptr, void* lds_base) {
   static_assert(BYTES == 16 || BYTES == 4, "fragment size");
@@ -143,13 +156,11 @@ __device__ __forceinline__ void select_top(const uint32_t (&u)[NG], int M0, int 
 
 // ---- workspace layout ---------------------------------------------------------
 // [0, align256(4*BH))         scale sigma of every (batch, head)
-// then kZeroBytes of zeros    (source of the codeword rows of padding children)
 // then per (batch, head), align256(bytes) each:
 //   parent value fragments    (M0p/32 blocks) x [KV][2][D] fragments
 //   child value fragments     M0 parents x [W/E][D] fragments
 // A fragment is E consecutive operand elements (8 fp16, or 1 fp32).
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr int kZeroBytes = 256;
 constexpr int kYRow = 36;  // floats per staged output row (32 dims + 4 to spread LDS banks)
 
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
@@ -157,7 +168,7 @@ size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   const size_t M0p = attn_parent_rows(M0);
   const size_t W = C <= 8 ? 8 : 16;
   const size_t per = align256((M0p * d + (size_t)M0 * W * d) * pes);
-  return align256((size_t)BH * 4) + kZeroBytes + (size_t)BH * per;
+  return align256((size_t)BH * 4) + (size_t)BH * per;
 }
 
 // Prep: one round of loads per thread.  Every block of a (batch, head) first
@@ -246,7 +257,6 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
     sig = value_scale(mx);
   }
   if (part == 0 && tid == 0) ((float*)ws)[bh] = sig;
-  if (blockIdx.x == 0 && tid < kZeroBytes / 4) ((float*)(ws + sig_bytes - kZeroBytes))[tid] = 0.0f;
   const float inv = 1.0f / sig;
   pvfrag_t* pf = (pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
 #pragma unroll
@@ -337,8 +347,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* Yb = Y + (int64_t)bh * N * D;
   const float sig = ((const float*)ws)[bh];
   const pvfrag_t* pvf = (const pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
-  const unsigned char* zeros = ws + sig_bytes - kZeroBytes;  // codeword rows past C
   const pvfrag_t* cvf = pvf + nblkP * FV;
+  // descriptors of the head's codebook and of the child value fragments
+  const __amdgpu_buffer_rsrc_t cb_rs = __builtin_amdgcn_make_buffer_rsrc((void*)cbh, 0, Mt * D * (int)sizeof(in_t), kBufWord3);
+  const __amdgpu_buffer_rsrc_t cv_rs = __builtin_amdgcn_make_buffer_rsrc((void*)cvf, 0, M0 * (W / E) * D * BV, kBufWord3);
   const int nPT = (M0 + 63) / 64;
 
   // ---- once per workgroup: parents into LDS -----------------------------------
@@ -570,7 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int cs = 0; cs < P; cs += NCB * S) {
         if (cs > 0) __syncthreads();  // readers of the previous chunk are done
         // codeword fragments: one DMA per (block, k-step); lane = (row, half).
-        // Slots past P and rows past C read zeros.
+        // Slots past P and rows past C read zeros (offsets out of range).
         {
           const int r = r_of_row(ql), hr = h_of_row(ql);
           const int s_row = 2 * (r / W) + hr, c_row = r % W;
@@ -578,8 +590,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             const int b = u / KS, s = u % KS;
             const int gs = cs + b * S + s_row;
             const bool ok = gs < P && c_row < C;
-            const in_t* src = cbh + (int64_t)(M0 + sel[ok ? gs : 0] * C + c_row) * D + s * 2 * E + E * hh;
-            lds_dma<BA>(ok ? (const void*)src : (const void*)zeros, sCC + u * 64);
+            const int voff = ((M0 + sel[ok ? gs : 0] * C + c_row) * D + s * 2 * E + E * hh) * (int)sizeof(in_t);
+            lds_dma_buf<BA>(cb_rs, ok ? voff : kOutOfRange, sCC + u * 64);
           }
         }
         // value fragments: one DMA per (block, k-step, half, 64 dims); lane = dim
@@ -589,7 +601,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const int r = k * E;
           const int gs = cs + b * S + 2 * (r / W) + h2, gg = (r % W) / E;
           const int p = gs < P ? sel[gs] : sel[0];
-          lds_dma<BV>(cvf + ((int64_t)p * (W / E) + gg) * D + dc * 64 + lane, sCV + ((b * KV + k) * 2 + h2) * D + dc * 64);
+          lds_dma_buf<BV>(cv_rs, (((p * (W / E) + gg) * D + dc * 64 + lane) * BV), sCV + ((b * KV + k) * 2 + h2) * D + dc * 64);
         }
         // counts and biases of the chunk's NCB * 32 = 64 rows (one per lane of
         // wave 0), and whether any row is empty (then the chunk takes masks)
@@ -755,7 +767,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
-  const size_t sig_bytes = align256((size_t)BH * 4) + kZeroBytes;
+  const size_t sig_bytes = align256((size_t)BH * 4);
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
   {
     constexpr int E = T::E, KV = 16 / E;
