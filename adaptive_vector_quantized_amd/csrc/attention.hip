@@ -407,6 +407,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int tile = tile0; tile < tile1; ++tile) {
     const int qi = tile * bq + wave * 32 + ql;
     const bool qv = qi < N;
+    // the next tile's queries, a whole tile ahead of their use
+    frag_t qn[KS];
+    {
+      const int qn_i = (tile + 1) * bq + wave * 32 + ql;
+      const in_t* qp = Qb + (int64_t)(qn_i < N ? qn_i : N - 1) * D + E * hh;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
+    }
 
     f32x16 xacc[DB];
 #pragma unroll
@@ -566,14 +574,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
     }
 
-    frag_t qn[KS];
-    auto prefetch_next = [&]() {
-      const int qn_i = (tile + 1) * bq + wave * 32 + ql;
-      const in_t* qp = Qb + (int64_t)(qn_i < N ? qn_i : N - 1) * D + E * hh;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
-    };
-    if (P == 0) prefetch_next();
 
     // children of the selected parents (Alg. 2 lines 10-19), CH rows per chunk
     if (P > 0) {
@@ -618,7 +618,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (cs == 0) prefetch_next();
         const bool chunk_masked = __builtin_amdgcn_readfirstlane(sFlag[1]) != 0;
 
         // logits of the whole chunk
