@@ -107,7 +107,7 @@ __device__ __forceinline__ float xhalf_max(float x) {
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <- 15 - i within 16
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- 7 - i within 8
@@ -116,40 +116,22 @@ constexpr int DPP_QP_1032 = 0xB1;           // lane i <- i ^ 1
 
 // Reduce-scatter over the 16 lanes of a DPP row: on entry v[0..16) per lane,
 // on exit v[0] of lane i holds the sum over the row of register (i % 16).
+// Each butterfly step forms both candidate sums with the partner's value
+// moved by DPP (folded into the add) and keeps the one for this lane's half.
+template <int CTRL, int HALF>
+__device__ __forceinline__ void rs_step(float* v, bool lo) {
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float a = v[i] + dpp<CTRL>(v[i]);                // kept by the lower lanes
+    const float b = v[HALF + i] + dpp<CTRL>(v[HALF + i]);  // kept by the upper lanes
+    v[i] = lo ? a : b;
+  }
+}
 __device__ __forceinline__ void rs_row16(float* v, int lane) {
-  {  // partner 15 - i: lanes i < 8 keep registers 0..7
-    const bool lo = (lane & 15) < 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float send = lo ? v[8 + i] : v[i];
-      float keep = lo ? v[i] : v[8 + i];
-      v[i] = keep + dpp<DPP_ROW_MIRROR>(send);
-    }
-  }
-  {
-    const bool lo = (lane & 7) < 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float send = lo ? v[4 + i] : v[i];
-      float keep = lo ? v[i] : v[4 + i];
-      v[i] = keep + dpp<DPP_ROW_HALF_MIRROR>(send);
-    }
-  }
-  {
-    const bool lo = (lane & 3) < 2;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      float send = lo ? v[2 + i] : v[i];
-      float keep = lo ? v[i] : v[2 + i];
-      v[i] = keep + dpp<DPP_QP_3210>(send);
-    }
-  }
-  {
-    const bool lo = (lane & 1) == 0;
-    float send = lo ? v[1] : v[0];
-    float keep = lo ? v[0] : v[1];
-    v[0] = keep + dpp<DPP_QP_1032>(send);
-  }
+  rs_step<DPP_ROW_MIRROR, 8>(v, (lane & 15) < 8);      // partner 15 - i
+  rs_step<DPP_ROW_HALF_MIRROR, 4>(v, (lane & 7) < 4);  // partner 7 - i within 8
+  rs_step<DPP_QP_3210, 2>(v, (lane & 3) < 2);          // partner 3 - i within 4
+  rs_step<DPP_QP_1032, 1>(v, (lane & 1) == 0);         // partner i ^ 1
 }
 
 // Sum over the 32 lanes of each half of 32 registers: on exit v[0] of lane l
