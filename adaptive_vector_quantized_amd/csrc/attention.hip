@@ -314,8 +314,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sNc = sNp + M0p;                                             // [CH]
   float* sBp = sNc + nCH;                                             // [M0p] 0 or -inf (empty)
   float* sBc = sBp + M0p;                                             // [CH]
-  float* sW = sBc + nCH;                                              // [nw][M0p]
-  int* sSel = (int*)(sW + (need_imp ? nw * M0p : 0));                 // [nw][Pp]
+  float* sW = sBc + nCH;                                              // [M0p][4] partials per wave
+  int* sSel = (int*)(sW + (need_imp ? M0p * 4 : 0));                  // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [2] all parents hold keys; chunk needs masks
   float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 2) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
 
@@ -363,6 +363,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
   for (int u = wave; u < nblkP * FV / 64; u += nw) lds_dma<BV>(pvf + u * 64 + lane, sPV + u * 64);
   if (tid == 0) sFlag[0] = 1;
+  // importance partials: slots of absent waves (and of parents past M0) stay zero
+  if (need_imp)
+    for (int i = tid; i < M0p * 4; i += nthreads) sW[i] = 0.0f;
   __syncthreads();
   for (int c = tid; c < M0p; c += nthreads) {
     const int j = parent_of_col(c);
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         rs_half32(t, lane);
         const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
         const float nj = parents_lds ? sNp[32 * (ql >> 4) + col_of(ql & 15, hh)] : 1.0f;
-        if (j < M0) sW[wave * M0p + j] = t[0] * nj;
+        if (j < M0) sW[j * 4 + wave] = t[0] * nj;
       }
       __syncthreads();
       // every wave forms the totals and its own copy of the selection
@@ -549,11 +552,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       for (int g = 0; g < MAXG; ++g) {
         const int j = g * 64 + lane;
         float s = 0.0f;
-        if (g * 64 < M0 && j < M0) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            if (w < nw) s += sW[w * M0p + j];
-          if (importance && wave == 0) importance[((int64_t)bh * ntiles + tile) * M0 + j] = s;
+        if (g * 64 < M0) {  // j < M0p
+          const f32x4 p4 = *(const f32x4*)(sW + j * 4);
+          s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+          if (importance && wave == 0 && j < M0) importance[((int64_t)bh * ntiles + tile) * M0 + j] = s;
         }
         u[g] = __float_as_uint(s);  // 0 past M0: never above a threshold search candidate
       }
@@ -736,7 +738,7 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   b += M0p * d * es;                          // parents' value fragments
   b += 2 * ch * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
-  if (P > 0 || importance) b += nw * M0p * 4;          // importance partials
+  if (P > 0 || importance) b += M0p * 4 * 4;           // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
   b = (b + 15) & ~(size_t)15;
   b += nw * 32 * kYRow * 4;                   // output staging
