@@ -706,6 +706,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
     }
 
+    // the next tile's queries, taken before this tile's output stores are
+    // issued (a wait for the loads then never waits for those stores)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = qn[s];
+
     // Y = x / z (Alg. 2 line 20).  A lane holds 4-float runs of its query's
     // row; the wave's output goes through LDS 32 dims at a time.
     const float zt = xhalf_sum(zp);
@@ -722,8 +727,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
       store_rows(q0, db);
     }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = qn[s];
   }
 }
 
