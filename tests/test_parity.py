@@ -71,6 +71,23 @@ def test_tiny_bf16():
     _full_check(_data("tiny", dtype="bf16"), 4)
 
 
+@pytest.mark.parametrize("dtype,P", [("f32", 4), ("f32", 12), ("bf16", 12)])
+def test_sparse_occupancy(dtype, P):
+    """Keys crowd into a few parents (Zipf s = 4 over 16 parents): most parents
+    and many children hold no keys, so the parent pass takes its -inf biases,
+    child chunks take their masks, selected parents can be empty, and with P
+    above the number of parents holding keys the top-P set ends in zero
+    importances, taken by the lower index."""
+    data = _data("tiny", dtype=dtype, parents="zipf", zipf_s=4.0)
+    o = oracle.Oracle.for_cfg(data["cfg"])
+    parent, _ = o.assign(data["K"], data["codebook"])
+    n_par = len(np.unique(parent))
+    assert n_par < data["cfg"].M0, "the case needs parents without keys"
+    if P == 12:
+        assert n_par < P, "the case needs fewer parents with keys than P"
+    _full_check(data, P)
+
+
 @pytest.mark.parametrize("seed", [1001, 5])
 def test_grid64(seed):
     _full_check(_data("grid64", seed=seed), 16)
