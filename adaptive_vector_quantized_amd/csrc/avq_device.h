@@ -144,13 +144,6 @@ __device__ __forceinline__ void rs_half32(float* v, int lane) {
   }
   rs_row16(v, lane);
 }
-// Same for 16 registers: on exit v[0] of lane l holds the half's total of
-// register (l % 16).
-__device__ __forceinline__ void rs_half16(float* v, int lane) {
-  rs_row16(v, lane);
-  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
-  v[0] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
