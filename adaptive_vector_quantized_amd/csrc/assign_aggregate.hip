@@ -93,23 +93,28 @@ struct AssignShape {
   static constexpr int KPW = 128 / kVgprPerKey;  // keys per wave: 64 registers of values
   static constexpr int kChunk = 4 * KPW;         // keys per workgroup
   static constexpr int LDP = D + 16 / (int)sizeof(typename T::in_t);  // padded LDS row of a parent
-  static constexpr int kWaves = (D == 64 && T::E > 1) ? 4 : 2;  // waves per SIMD the registers are set for
+  static constexpr int ACC_D = D < 64 ? D : 64;  // value columns per pass of the partial tiles
+  // waves per SIMD the registers are set for: parents in LDS, or read from L2
+  static constexpr int kWavesLds = (D == 64 && T::E > 1) ? 4 : 2;
+  static constexpr int kWavesL2 = T::E > 1 ? (D == 64 ? 4 : 3) : (D == 64 ? 3 : 2);
 };
 
-static AssignLds assign_lds(int es, int d, int M0, int C, int chunk) {
+// parents_lds: the parents' codewords are staged in LDS (else read from L2)
+static AssignLds assign_lds(int es, int d, int M0, int C, int chunk, bool parents_lds) {
   const size_t M0p = (M0 + 31) & ~31;
   const size_t Mt = (size_t)M0 * (1 + C);
   const size_t NB = (size_t)M0 * (C + 1);
   const size_t ldp = d + 16 / es;
   size_t o = 0, at[12];
   // assignment phase only
-  at[0] = o; o = al16(o + M0p * ldp * es);         // parents, padded rows
+  at[0] = o; o = al16(o + (parents_lds ? M0p * ldp * es : 0));  // parents, padded rows
   at[1] = o; o = al16(o + M0p * 4);                // parent norms
   at[2] = o; o = al16(o + 4 * 32 * 4);             // child-block norms, per wave
   at[3] = o; o = al16(o + 4 * 64 * 4);             // distinct parents of a wave step
-  // aggregation phase only: four partial value tiles over the same bytes
+  // aggregation phase only: four partial value tiles (up to 64 columns) over
+  // the same bytes
   at[9] = 0;
-  o = std::max(o, al16((size_t)4 * 32 * d * 4));
+  o = std::max(o, al16((size_t)4 * 32 * (d < 64 ? d : 64) * 4));
   at[4] = o; o = al16(o + NB * 4);                 // key count per (parent, child slot)
   at[5] = o; o = al16(o + 8 * 4);                  // scan partials
   at[6] = o; o = al16(o + Mt * 2);                 // codeword -> slot
@@ -125,8 +130,11 @@ static AssignLds assign_lds(int es, int d, int M0, int C, int chunk) {
 }
 
 // W: width of a child slot in accumulator registers (C <= W, W in {4,8,16}).
-template <class T, int D, int W>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(AssignShape<T, D>::kWaves))) void
+// PL: parents' codewords staged in LDS; else read from L2 by the MFMA loop
+// (large codebooks: the LDS then holds more workgroups per CU).
+template <class T, int D, int W, bool PL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PL ? AssignShape<T, D>::kWavesLds
+                                                                          : AssignShape<T, D>::kWavesL2))) void
 assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T::in_t* __restrict__ V,
                         const typename T::in_t* __restrict__ cb, int H, int N, int M0, int C,
                         AssignLds L, float* __restrict__ vsum, int* __restrict__ counts, int* __restrict__ assign) {
@@ -168,17 +176,19 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   const in_t* Kb = K + (int64_t)bh * N * D;
   const in_t* Vb = V + (int64_t)bh * N * D;
 
-  // ---- stage parents, clear the histogram, parent norms from LDS ---------
-  for (int i = tid; i < M0p * (D / E); i += 256) {
-    const int row = i / (D / E), col = (i % (D / E)) * E;
-    const int src = row < M0 ? row : 0;
-    *(frag_t*)(sPar + row * LDP + col) = *(const frag_t*)(cbh + (int64_t)src * D + col);
+  // ---- stage parents, clear the histogram, parent norms -----------------
+  if constexpr (PL) {
+    for (int i = tid; i < M0p * (D / E); i += 256) {
+      const int row = i / (D / E), col = (i % (D / E)) * E;
+      const int src = row < M0 ? row : 0;
+      *(frag_t*)(sPar + row * LDP + col) = *(const frag_t*)(cbh + (int64_t)src * D + col);
+    }
   }
   for (int i = tid; i < NB; i += 256) sHist[i] = 0;
   __syncthreads();
   for (int i = tid; i < M0p * 4; i += 256) {  // 4 lanes per row; M0p * 4 is a multiple of 64
     const int row = i >> 2, q = i & 3;
-    const in_t* pr = sPar + row * LDP + q * (D / 4);
+    const in_t* pr = PL ? sPar + row * LDP + q * (D / 4) : cbh + (int64_t)(row < M0 ? row : 0) * D + q * (D / 4);
     float acc = 0.0f;
 #pragma unroll
     for (int t = 0; t < D / 4; t += E) acc = frag_sumsq<T>(*(const frag_t*)(pr + t), acc);
@@ -213,7 +223,9 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     int bidx[2] = {0, 0};
     for (int blk = 0; blk < nblkP; ++blk) {
       f32x16 a0 = zero16(), a1 = zero16();
-      const in_t* ap = sPar + (blk * 32 + ql) * LDP + E * hh;
+      // rows past M0 (norm +inf) are never chosen; from L2 they repeat row M0 - 1
+      const in_t* ap = PL ? sPar + (blk * 32 + ql) * LDP + E * hh
+                          : cbh + (int64_t)min(blk * 32 + ql, M0 - 1) * D + E * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         frag_t a = *(const frag_t*)(ap + s * 2 * E);
@@ -400,7 +412,9 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // one-hot A operand of the wave in LDS, over the bytes of its partial tile:
   // [half][k-step][slot row][E keys] (bf16 1.0 or 0; fp32 for E = 1)
   using oh_t = typename std::conditional<E == 8, unsigned short, float>::type;
-  oh_t* oh = (oh_t*)(tile + wave * 32 * D);
+  constexpr int ACC_D = Sh::ACC_D;    // columns of a partial tile per pass
+  constexpr int NPASS = D / ACC_D;
+  oh_t* oh = (oh_t*)(tile + wave * 32 * ACC_D);
   constexpr int OHN = 2 * KH * 32;  // entries
   for (int sb = 0; sb * 32 < nslots; ++sb) {
     // clear, then every key marks the rows of its parent and child slots
@@ -456,26 +470,32 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
       }
     }
     // partial tile of this wave (over its one-hot operand): row = slot within
-    // the block, col = dim
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float* tr = tile + (wave * 32 + row_of(r, hh)) * D + EPL * ql;
-      if constexpr (EPL == 2) {
-        *(f32x2*)tr = f32x2{acc[0][r], acc[1][r]};
-      } else {
-        *(f32x4*)tr = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-      }
-    }
-    __syncthreads();
-    // one row per wave instruction: consecutive lanes, consecutive floats
+    // the block, col = dim; ACC_D dims per pass (lane ql holds dims EPL*ql ..)
     const int nrow = min(32, nslots - 32 * sb);
-    for (int i = tid; i < nrow * D; i += 256) {
-      const int row = i / D, c = i % D;
-      float sum = tile[row * D + c];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) sum += tile[(w * 32 + row) * D + c];
-      atomic_add_f32(vsb + (int64_t)sRow[32 * sb + row] * D + c, sum);
+    for (int pass = 0; pass < NPASS; ++pass) {
+      if (pass > 0) __syncthreads();  // the previous pass's tiles are summed
+      __builtin_amdgcn_wave_barrier();
+      if (NPASS == 1 || (EPL * ql) / ACC_D == pass) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* tr = tile + (wave * 32 + row_of(r, hh)) * ACC_D + (EPL * ql) % ACC_D;
+          if constexpr (EPL == 2) {
+            *(f32x2*)tr = f32x2{acc[0][r], acc[1][r]};
+          } else {
+            *(f32x4*)tr = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+          }
+        }
+      }
+      __syncthreads();
+      // one row per wave instruction: consecutive lanes, consecutive floats
+      for (int i = tid; i < nrow * ACC_D; i += 256) {
+        const int row = i / ACC_D, c = i % ACC_D;
+        float sum = tile[row * ACC_D + c];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum += tile[(w * 32 + row) * ACC_D + c];
+        atomic_add_f32(vsb + (int64_t)sRow[32 * sb + row] * D + pass * ACC_D + c, sum);
+      }
     }
     if ((sb + 1) * 32 < nslots) __syncthreads();  // the next block rewrites the tiles
   }
@@ -500,21 +520,39 @@ __global__ __launch_bounds__(256) void zero_kernel(f32x4* __restrict__ a, int64_
 }
 
 template <class T, int D>
-static AssignLds lds_of(int M0, int C) {
-  return assign_lds((int)sizeof(typename T::in_t), D, M0, C, AssignShape<T, D>::kChunk);
+static AssignLds lds_of(int M0, int C, bool parents_lds) {
+  return assign_lds((int)sizeof(typename T::in_t), D, M0, C, AssignShape<T, D>::kChunk, parents_lds);
+}
+
+// Parents in LDS unless reading them from L2 at least doubles the workgroups
+// that share a CU (a workgroup puts one wave on each SIMD, so waves per SIMD
+// = workgroups); the L2 reads cost more than one extra workgroup gains.
+template <class T, int D>
+static bool parents_in_lds(int M0, int C) {
+  constexpr size_t kLdsPerCu = 160 * 1024;
+  using Sh = AssignShape<T, D>;
+  const size_t lp = lds_of<T, D>(M0, C, true).total, lg = lds_of<T, D>(M0, C, false).total;
+  const size_t wp = std::min<size_t>(kLdsPerCu / lp, Sh::kWavesLds);
+  const size_t wg = std::min<size_t>(kLdsPerCu / lg, Sh::kWavesL2);
+  return wg < 2 * wp;
+}
+
+template <class T, int D>
+static size_t smem_of(int M0, int C) {
+  return lds_of<T, D>(M0, C, parents_in_lds<T, D>(M0, C)).total;
 }
 
 size_t assign_smem_bytes(int dtype, int d, int M0, int C) {
-  if (dtype == 0) return d == 64 ? lds_of<TF32, 64>(M0, C).total : lds_of<TF32, 128>(M0, C).total;
-  return d == 64 ? lds_of<TBF16, 64>(M0, C).total : lds_of<TBF16, 128>(M0, C).total;
+  if (dtype == 0) return d == 64 ? smem_of<TF32, 64>(M0, C) : smem_of<TF32, 128>(M0, C);
+  return d == 64 ? smem_of<TBF16, 64>(M0, C) : smem_of<TBF16, 128>(M0, C);
 }
 
-template <class T, int D, int W>
+template <class T, int D, int W, bool PL>
 static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, int BH, int H, int N, int M0, int C,
                                   float* vsum, int* counts, int* assign, hipStream_t st) {
   using Sh = AssignShape<T, D>;
-  const AssignLds L = lds_of<T, D>(M0, C);
-  auto kern = assign_aggregate_kernel<T, D, W>;
+  const AssignLds L = lds_of<T, D>(M0, C, PL);
+  auto kern = assign_aggregate_kernel<T, D, W, PL>;
   hipError_t e = raise_lds_limit((const void*)kern, L.total);
   if (e != hipSuccess) return e;
   dim3 grid((N + Sh::kChunk - 1) / Sh::kChunk, BH);
@@ -526,9 +564,14 @@ static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, 
 template <class T, int D>
 static hipError_t launch_assign_w(const void* K, const void* V, const void* cb, int BH, int H, int N, int M0, int C,
                                   float* vsum, int* counts, int* assign, hipStream_t st) {
-  if (C <= 4) return launch_assign_t<T, D, 4>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-  if (C <= 8) return launch_assign_t<T, D, 8>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-  return launch_assign_t<T, D, 16>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  if (parents_in_lds<T, D>(M0, C)) {
+    if (C <= 4) return launch_assign_t<T, D, 4, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+    if (C <= 8) return launch_assign_t<T, D, 8, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+    return launch_assign_t<T, D, 16, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  }
+  if (C <= 4) return launch_assign_t<T, D, 4, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  if (C <= 8) return launch_assign_t<T, D, 8, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  return launch_assign_t<T, D, 16, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
 }
 
 hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st) {
