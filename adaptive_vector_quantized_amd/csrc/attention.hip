@@ -410,14 +410,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   for (int tile = tile0; tile < tile1; ++tile) {
     const int qi = tile * bq + wave * 32 + ql;
     const bool qv = qi < N;
-    // the next tile's queries, a whole tile ahead of their use
+    // the next tile's queries, a whole tile ahead of their use (d = 64; at
+    // d = 128 they are loaded at the end of the tile, saving registers)
+    constexpr bool kEarlyQ = D == 64;
     frag_t qn[KS];
-    {
+    auto load_next_q = [&]() {
       const int qn_i = (tile + 1) * bq + wave * 32 + ql;
       const in_t* qp = Qb + (int64_t)(qn_i < N ? qn_i : N - 1) * D + E * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
-    }
+    };
+    if constexpr (kEarlyQ) load_next_q();
 
     f32x16 xacc[DB];
 #pragma unroll
@@ -708,6 +711,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
     // the next tile's queries, taken before this tile's output stores are
     // issued (a wait for the loads then never waits for those stores)
+    if constexpr (!kEarlyQ) load_next_q();
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qn[s];
 
