@@ -113,36 +113,13 @@ def test_tiled_parents(M0, P):
     _full_check(_data("grid64", M0=M0, H=2, N=2048 + 64 + 5, grid=None), P)
 
 
-def test_tiled_parents_d128():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiled_parents_d128(dtype):
     """d = 128 with 256 parents (the 256x256-grid shape at small N): the assign
     kernel reads the parents from L2 and adds its partial tiles 64 columns at a
-    time; the attention kernel takes the two-pass denominator."""
-    _full_check(_data("grid64", d=128, M0=256, H=2, N=2048 + 64 + 5, grid=None), 32)
-
-
-def test_assign_d128_fp32_large_codebook():
-    """The assign kernel alone on fp32 inputs, d = 128, 256 parents (parents
-    from L2, two 64-column passes); the attention call does not take this
-    size in fp32 (its parent values would not fit in LDS) and reports so."""
-    import torch
-    from adaptive_vector_quantized_amd import _lib
-    from parity_util import to_device
-    data = _data("grid64", d=128, M0=256, H=2, N=2048 + 64 + 5, grid=None, dtype="f32")
-    cfg = data["cfg"]
-    K = to_device(data["K"], cfg.dtype, cfg.B, cfg.H)
-    V = to_device(data["V"], cfg.dtype, cfg.B, cfg.H)
-    cb = torch.from_numpy(data["codebook"]).contiguous().cuda()
-    vsum, counts, assign = _lib.assign_aggregate(K, V, cb, cfg.C, want_assign=True)
-    torch.cuda.synchronize()
-    o = oracle.Oracle.for_cfg(cfg)
-    parent, row = o.assign(data["K"], data["codebook"])
-    assert np.array_equal(assign.cpu().numpy().reshape(cfg.BH, cfg.N), row)
-    ovsum, ocounts = o.aggregate(data["V"], parent, row)
-    assert np.array_equal(counts.cpu().numpy().reshape(cfg.BH, cfg.Mt), ocounts)
-    vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
-    check_vsum(vsum.cpu().numpy().reshape(cfg.BH, cfg.Mt, cfg.d), ovsum, vabs, ocounts)
-    with pytest.raises(_lib.AvqError):
-        _lib.attention_fwd(to_device(data["Q"], cfg.dtype, cfg.B, cfg.H), cb, vsum, counts, cfg.C, 32, cfg.block_q, cfg.scale)
+    time; the attention kernel reads the parents' codewords and values from L2
+    and takes the two-pass denominator."""
+    _full_check(_data("grid64", d=128, M0=256, H=2, N=2048 + 64 + 5, grid=None, dtype=dtype), 32)
 
 
 @pytest.mark.parametrize("M0", [64, 256])
