@@ -270,9 +270,10 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   }
 }
 
-// PL: the parents' codewords and value fragments are held in LDS (M0 <= 64);
-// else the codewords are read from L2 one block ahead of their MFMAs and the
-// value fragments from L2 at their MFMAs (the LDS then holds two workgroups)
+// PL: the parents' codewords are held in LDS (M0 <= 64); else they are read
+// from L2 one block ahead of their MFMAs.  The parents' value fragments are
+// held in LDS too, except at d = 128 with more than 64 parents, where they are
+// read from L2 at their MFMAs (the LDS then holds two workgroups)
 template <class T, int D, int W, bool PL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
@@ -303,13 +304,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int nblkP = M0p / 32;
   const int Pp = P > 0 ? P : 1;
   constexpr bool parents_lds = PL;
+  constexpr bool values_lds = PL || D == 64;
   frag_t* sPC = (frag_t*)smem;                                        // [nblkP*FA] if parents_lds
-  pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV] if parents_lds
+  pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV] if values_lds
   // the children's arrays exist only when P > 0, the importance partials only
   // when importances are formed
   const bool need_imp = (P > 0) || (importance != nullptr);
   const int nCB = P > 0 ? NCB : 0, nCH = P > 0 ? CH : 0;
-  frag_t* sCC = (frag_t*)(sPV + (parents_lds ? nblkP * FV : 0));      // [NCB*FA]
+  frag_t* sCC = (frag_t*)(sPV + (values_lds ? nblkP * FV : 0));       // [NCB*FA]
   pvfrag_t* sCV = (pvfrag_t*)(sCC + nCB * FA);                        // [NCB*FV]
   float* sNp = (float*)(sCV + nCB * FV);                              // [M0p] counts
   float* sNc = sNp + M0p;                                             // [CH]
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       lds_dma<BA>(cbh + (int64_t)(j < M0 ? j : 0) * D + s * 2 * E + E * hh, sPC + u * 64);
     }
   }
-  if constexpr (parents_lds)
+  if constexpr (values_lds)
     for (int u = wave; u < nblkP * FV / 64; u += nw) lds_dma<BV>(pvf + u * 64 + lane, sPV + u * 64);
   if (tid == 0) sFlag[0] = 1;
   // importance partials: slots of absent waves (and of parents past M0) stay zero
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const pvfrag_t bf = pv_operand<T, KV>(lg[b], k);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            xacc[db] = T::mma_pv((parents_lds ? sPV : pvf)[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
+            xacc[db] = T::mma_pv((values_lds ? sPV : pvf)[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
         }
       }
     }
@@ -744,7 +746,7 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   (void)C;
   const size_t ch = P > 0 ? CH : 0;
   size_t b = (M0p <= 64 ? M0p * d * es : 0);  // parents' codeword fragments
-  if (M0p <= 64) b += M0p * d * es;           // parents' value fragments (else read from L2)
+  if (M0p <= 64 || d == 64) b += M0p * d * es;  // parents' value fragments (else read from L2)
   b += 2 * ch * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
   if (P > 0 || importance) b += M0p * 4 * 4;           // importance partials
