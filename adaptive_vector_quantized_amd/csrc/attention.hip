@@ -15,8 +15,10 @@
 //  2. attention_kernel.  A workgroup owns a contiguous range of query tiles
 //     of one (batch, head); one wave handles 32 queries of a tile.  The
 //     parents' codeword and value fragments are copied into LDS once per
-//     workgroup; per tile, the selected parents' children are copied into LDS
-//     by asynchronous global-to-LDS loads (no registers held, one wait).
+//     workgroup (up to 64 parents; beyond, the codewords, and at d = 128 also
+//     the value fragments, are read from L2); per tile, the selected
+//     parents' children are copied into LDS by asynchronous buffer loads (no
+//     registers held, one wait).  The output goes out in streaming stores.
 //
 // Per tile.  Logits are computed transposed on MFMA (rows = codewords,
 // columns = queries): each lane owns one query and 16 codewords per 32-row
