@@ -6,8 +6,9 @@
 // head).  Design for CDNA4:
 //   * Parent distances ||c||^2 - 2 k.c come from MFMA: parents of the head
 //     are staged once in LDS as the A operand (their norms are reduced from
-//     LDS), keys are streamed from HBM straight into B-operand registers (64
-//     keys per wave step) and stay there for the child search.
+//     LDS; a large codebook is read from L2 instead when that fits more
+//     workgroups on a CU), keys are streamed from HBM straight into B-operand
+//     registers (64 keys per wave step) and stay there for the child search.
 //   * Child distances: the distinct parents of the wave's 64 keys are packed
 //     S = 32 / W at a time into a 32-row block of their children, one MFMA
 //     block per group; the children's norms come from the same operand
