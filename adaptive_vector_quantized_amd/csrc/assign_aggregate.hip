@@ -186,7 +186,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     }
   }
   for (int i = tid; i < NB; i += 256) sHist[i] = 0;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < M0p * 4; i += 256) {  // 4 lanes per row; M0p * 4 is a multiple of 64
     const int row = i >> 2, q = i & 3;
     const in_t* pr = PL ? sPar + row * LDP + q * (D / 4) : cbh + (int64_t)(row < M0 ? row : 0) * D + q * (D / 4);
@@ -197,7 +197,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     acc += __shfl_xor(acc, 2);
     if (q == 0) sNorm[row] = row < M0 ? acc : INFINITY;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- assignment, 64 keys per wave step ---------------------------------
   const int nblkP = M0p / 32;
@@ -355,7 +355,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
 #pragma unroll
     for (int u = 0; u < KH; ++u) vr[u] = buf_load<raw_t>(rs, voff, u * D * (int)sizeof(in_t));
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- slots: thread p owns parent p (M0 <= 256) and its C children -------
   int nz = 0, pcount = 0;
@@ -370,7 +370,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   }
   const int incl = wave_incl_scan(nz, lane);
   if (lane == 63) sScan[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int off = incl - nz;
   int nslots = 0;
 #pragma unroll
@@ -390,7 +390,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // slots of every key: parent slot | child slot << 16 (0xFFFF: the key stayed)
   for (int k = tid; k < nval; k += 256) {
     const int x = sBin[k];
@@ -398,7 +398,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     const uint32_t cs = sl ? (uint32_t)sSlot[M0 + p * C + sl - 1] : 0xFFFFu;
     sKS[k] = (uint32_t)sSlot[p] | (cs << 16);
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- value sums on MFMA: (one-hot of key -> slot)^T x V -------------------
   // Slots are taken 32 at a time (M = slots).  K = keys: a k-step takes E
@@ -475,7 +475,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     const int nrow = min(32, nslots - 32 * sb);
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {
-      if (pass > 0) __syncthreads();  // the previous pass's tiles are summed
+      if (pass > 0) lds_barrier();  // the previous pass's tiles are summed
       __builtin_amdgcn_wave_barrier();
       if (NPASS == 1 || (EPL * ql) / ACC_D == pass) {
 #pragma unroll
@@ -488,7 +488,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       // one row per wave instruction: consecutive lanes, consecutive floats
       for (int i = tid; i < nrow * ACC_D; i += 256) {
         const int row = i / ACC_D, c = i % ACC_D;
@@ -498,7 +498,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
         atomic_add_f32(vsb + (int64_t)sRow[32 * sb + row] * D + pass * ACC_D + c, sum);
       }
     }
-    if ((sb + 1) * 32 < nslots) __syncthreads();  // the next block rewrites the tiles
+    if ((sb + 1) * 32 < nslots) lds_barrier();  // the next block rewrites the tiles
   }
 
   // ---- counts --------------------------------------------------------------

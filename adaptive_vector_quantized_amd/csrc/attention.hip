@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         const float nj = parents_lds ? sNp[32 * (ql >> 4) + col_of(ql & 15, hh)] : 1.0f;
         if (j < M0) sW[j * 4 + wave] = t[0] * nj;
       }
-      __syncthreads();
+      lds_barrier();
       // every wave forms the totals and its own copy of the selection
       constexpr int MAXG = 4;  // up to 256 parents, one per lane per group
       uint32_t u[MAXG];
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         }
         __builtin_amdgcn_wave_barrier();
       } else {
-        __syncthreads();  // partials are rewritten by the next tile; no staging barrier follows
+        lds_barrier();  // partials are rewritten by the next tile; no staging barrier follows
       }
     }
 
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       const int* sel = sSel + wave * Pp;
       const float sl2C = sl2 / (float)C;  // Eq. 8's mean folded into the logit scale
       for (int cs = 0; cs < P; cs += NCB * S) {
-        if (cs > 0) __syncthreads();  // readers of the previous chunk are done
+        if (cs > 0) lds_barrier();  // readers of the previous chunk are done
         // codeword fragments: one DMA per (block, k-step); lane = (row, half).
         // Slots past P and rows past C read zeros (offsets out of range).
         {
@@ -627,8 +627,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           const bool any_empty = __builtin_amdgcn_ballot_w64(!(n > 0.0f)) != 0;
           if (lane == 0) sFlag[1] = any_empty ? 1 : 0;
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's staging copies have landed
+        lds_barrier();
         const bool chunk_masked = __builtin_amdgcn_readfirstlane(sFlag[1]) != 0;
 
         // logits of the whole chunk

@@ -161,4 +161,13 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) { unsafeAtomicAdd(p, v); }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are complete
+// before it and visible after it.  Unlike __syncthreads() it does not wait for
+// the wave's global loads and stores still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace avq
