@@ -5,7 +5,7 @@ per-head hierarchical codebooks, keys from a spatially smooth cluster mixture,
 queries and values, with the shapes and structure of the image-token workloads
 the paper times (ViT / DPT / SD1.5 token grids; Sec. 5, Sec. E, Tab. 2).
 
-Construction (the readings behind each choice are listed in the design doc):
+Construction:
 
 * Codebook, per head (Sec. 4.1 and Eq. 5: each parent equals the mean of its
   children).  Draw p0 ~ N(0, I) and raw children r_c = p0 + 0.3 N(0, I).  Put

@@ -129,8 +129,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the forward pass shards over batch*heads with no communication; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported (the forward pass "
+              "would shard over batch*heads, each GPU running both calls on its share with no "
+              "communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch
