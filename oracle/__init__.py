@@ -42,6 +42,7 @@ def load(path: Optional[str] = None):
     lib.avqo_aggregate.argtypes = [i32] * 6 + [P, P, P, P, P]
     lib.avqo_importance.argtypes = [i32] * 6 + [P, P, P, i32, dbl, P]
     lib.avqo_importance_f64.argtypes = [i32] * 6 + [P, P, P, i32, dbl, P]
+    lib.avqo_importance_tiled_f64.argtypes = [i32] * 6 + [P, P, P, i32, dbl, i32, P]
     lib.avqo_select.argtypes = [i64, i32, i32, P, P]
     for f in (lib.avqo_attention_alg2, lib.avqo_attention_substituted):
         f.argtypes = [i32] * 6 + [P, P, P, P, P, i32, i32, dbl, P]
@@ -121,6 +122,14 @@ class Oracle:
         Q, cb, counts = _f64(Q), _f64(codebook), _i32(counts)
         w = np.zeros((self.B * self.H, self.tiles(bq), self.M0), np.float64)
         _ok(self.lib.avqo_importance_f64(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, _p(w)))
+        return w
+
+    def importance_tiled_f64(self, Q, codebook, counts, bq: int, scale: float, tile: int):
+        """App. B (Eq. 13-14): importance with the approximate denominator over
+        codeword tiles of ``tile`` parents."""
+        Q, cb, counts = _f64(Q), _f64(codebook), _i32(counts)
+        w = np.zeros((self.B * self.H, self.tiles(bq), self.M0), np.float64)
+        _ok(self.lib.avqo_importance_tiled_f64(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, tile, _p(w)))
         return w
 
     # Alg. 2 line 9

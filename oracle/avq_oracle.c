@@ -34,6 +34,9 @@
  *   avqo_aggregate            column sums, parent/child count relations
  *   avqo_importance(_f64)     two-parent closed form; w >= 0, w = 0 iff n = 0,
  *                             sum of w over a tile = its query count
+ *   avqo_importance_tiled_f64 first codeword tile holds |I| * N_seen / N of the
+ *                             mass; one-codeword tiles: w_0 = |I| n_0 / N; the
+ *                             last tile's parents get the exact Eq. 7 values
  *   avqo_select               hand cases with ties, brute-force sort
  *   avqo_attention_*          the three output forms agree; keys = parents and
  *                             keys = children give exact softmax; linearity,
@@ -581,6 +584,65 @@ int avqo_importance_f64(int B, int H, int N, int d, int M0, int C,
             importance_tile_f64(i1 - i0, d, M0, Q + ((int64_t)bh * N + i0) * d,
                                 cb + (int64_t)h * Mt * d, counts + (int64_t)bh * Mt, scale, s,
                                 w + ((int64_t)bh * T + t) * M0);
+        }
+        free(s);
+    }
+    return ORACLE_OK;
+}
+
+/* App. B, Eq. 13-14: importance with the approximate tiled denominator, in
+ * double.  The parents are visited in tiles of `tile` consecutive codewords
+ * (tile J holds parents J*tile ... min(M0, (J+1)*tile) - 1).  After tile J:
+ *   N_seen(J) = sum of n_j over the parents of the tiles t <= J,
+ *   Z~_i(J)   = N / N_seen(J) * sum over t <= J of Z_i(t),
+ *               Z_i(t) = sum over j in t of A_ij n_j,
+ *   w_j       = sum over the queries i of the tile of A_ij n_j / Z~_i(J), j in J,
+ * with N the sum of n_j over all parents, A_ij = exp(s_ij - m_i), m_i the
+ * running maximum over the non-empty parents seen so far (the ratio A / Z~
+ * does not depend on it), A_ij = 0 where n_j = 0, and w_j = 0 while
+ * N_seen(J) = 0.  With one tile (tile >= M0) this is Eq. 7.  w: [BH][T][M0]. */
+int avqo_importance_tiled_f64(int B, int H, int N, int d, int M0, int C,
+                              const double* Q, const double* cb, const int32_t* counts,
+                              int bq, double scale, int tile, double* w) {
+    if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 0 || bq < 1 || tile < 1) return ORACLE_ERR;
+    const int64_t Mt = mt_of(M0, C);
+    const int BH = B * H, T = ntiles(N, bq);
+#pragma omp parallel for schedule(static)
+    for (int bh = 0; bh < BH; ++bh) {
+        const int h = bh % H;
+        const double* cbh = cb + (int64_t)h * Mt * d;
+        const int32_t* n = counts + (int64_t)bh * Mt;
+        double* s = (double*)malloc(sizeof(double) * M0);
+        double ntot = 0.0;
+        for (int j = 0; j < M0; ++j) ntot += n[j];
+        for (int t = 0; t < T; ++t) {
+            double* wt = w + ((int64_t)bh * T + t) * M0;
+            for (int j = 0; j < M0; ++j) wt[j] = 0.0;
+            const int i_end = (t + 1) * bq < N ? (t + 1) * bq : N;
+            for (int i = t * bq; i < i_end; ++i) {
+                const double* q = Q + ((int64_t)bh * N + i) * d;
+                for (int j = 0; j < M0; ++j) s[j] = scale * dotd(q, cbh + (int64_t)j * d, d);
+                double m = -INFINITY, zacc = 0.0, nseen = 0.0;
+                for (int j0 = 0; j0 < M0; j0 += tile) {
+                    const int j1 = j0 + tile < M0 ? j0 + tile : M0;
+                    double mt = m;
+                    for (int j = j0; j < j1; ++j) {
+                        nseen += n[j];
+                        if (n[j] > 0 && s[j] > mt) mt = s[j];
+                    }
+                    if (mt > m) {  /* new stabiliser: rescale what is accumulated */
+                        zacc = m == -INFINITY ? 0.0 : zacc * exp(m - mt);
+                        m = mt;
+                    }
+                    for (int j = j0; j < j1; ++j)
+                        if (n[j] > 0) zacc += exp(s[j] - m) * n[j];
+                    if (nseen > 0.0) {
+                        const double zt = ntot / nseen * zacc;  /* Eq. 13 */
+                        for (int j = j0; j < j1; ++j)
+                            if (n[j] > 0) wt[j] += exp(s[j] - m) * n[j] / zt;  /* Eq. 14 */
+                    }
+                }
+            }
         }
         free(s);
     }

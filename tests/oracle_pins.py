@@ -399,6 +399,37 @@ def pin_flat_codebook(lib):
     np.testing.assert_allclose(flat["Y_alg2"], two["Y"], rtol=0, atol=1e-12)
 
 
+def pin_importance_tiled(lib):
+    """App. B (Eq. 13-14) on closed forms: the first codeword tile receives
+    |I| * N_seen(0) / N of the importance mass (its extrapolated denominator
+    is N / N_seen times its own partial sum); with one-codeword tiles the first
+    parent gets |I| n_0 / N whatever the logits; the parents of the last tile
+    see the complete denominator and get Eq. 7's values; one tile is Eq. 7;
+    w >= 0 and w = 0 where n = 0."""
+    cfg, data = _small_case(31, N=96, d=8, M0=6, C=3)
+    o = _O(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C)
+    parent, row = o.assign(data["K"], data["codebook"])
+    _, counts = o.aggregate(data["V"], parent, row)
+    bq, scale, M0 = cfg.block_q, cfg.scale, cfg.M0
+    Q, cb = data["Q"], data["codebook"]
+    exact = o.importance_f64(Q, cb, counts, bq, scale)
+    nq = np.array([min(cfg.N, (t + 1) * bq) - t * bq for t in range(o.tiles(bq))], np.float64)
+    n = counts[:, :M0].astype(np.float64)
+    ntot = n.sum(axis=1)
+    for tile in (1, 2, 4):
+        w = o.importance_tiled_f64(Q, cb, counts, bq, scale, tile)
+        assert np.all(w >= 0.0) and np.all(w[n[:, None, :].repeat(w.shape[1], 1) == 0] == 0.0)
+        nseen0 = n[:, :tile].sum(axis=1)
+        for bh in range(cfg.BH):
+            if nseen0[bh] > 0:
+                np.testing.assert_allclose(w[bh, :, :tile].sum(axis=1), nq * nseen0[bh] / ntot[bh], rtol=1e-12)
+            if tile == 1 and n[bh, 0] > 0:
+                np.testing.assert_allclose(w[bh, :, 0], nq * n[bh, 0] / ntot[bh], rtol=1e-12)
+        last = ((M0 - 1) // tile) * tile
+        np.testing.assert_allclose(w[:, :, last:], exact[:, :, last:], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(o.importance_tiled_f64(Q, cb, counts, bq, scale, M0), exact, rtol=1e-12, atol=1e-15)
+
+
 PINS = {
     "assign_ground_truth": pin_assign_ground_truth,
     "assign_copies": pin_assign_copies,
@@ -416,4 +447,5 @@ PINS = {
     "exact_attention": pin_exact_attention,
     "margins": pin_margins,
     "flat_codebook": pin_flat_codebook,
+    "importance_tiled": pin_importance_tiled,
 }

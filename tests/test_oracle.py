@@ -41,6 +41,11 @@ MUTANTS = [
     ("no residual for a refined parent", "nn[a] -= n[c0 + c];", ";"),
     ("brute force ignores the selection", "int32_t khat = (r != a && in_sel(S, P, a)) ? r : a;",
      "int32_t khat = r;"),
+    ("tiled denominator not extrapolated", "const double zt = ntot / nseen * zacc;", "const double zt = zacc;"),
+    ("tiled denominator not rescaled with the stabiliser", "zacc = m == -INFINITY ? 0.0 : zacc * exp(m - mt);",
+     "zacc = m == -INFINITY ? 0.0 : zacc;"),
+    ("keys of a tile's first parent not seen", "                        nseen += n[j];",
+     "                        nseen += (j > j0) ? n[j] : 0;"),
 ]
 
 
