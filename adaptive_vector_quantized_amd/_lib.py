@@ -38,8 +38,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.avq_assign_aggregate.argtypes = [P, P, P] + [i32] * 7 + [P, P, P, P]
     lib.avq_assign_aggregate.restype = i32
-    lib.avq_attention_fwd.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P, ctypes.c_size_t, P]
-    lib.avq_attention_fwd.restype = i32
+    for f in (lib.avq_attention_fwd, lib.avq_attention_fwd_approx):
+        f.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P, ctypes.c_size_t, P]
+        f.restype = i32
     lib.avq_attention_workspace_size.argtypes = [i32] * 6
     lib.avq_attention_workspace_size.restype = ctypes.c_size_t
     lib.avq_status_string.argtypes = [i32]
@@ -120,10 +121,11 @@ def workspace_size(B: int, H: int, d: int, M0: int, C: int, dtype: torch.dtype) 
 def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, counts: torch.Tensor, C: int, P: int,
                   block_q: int, scale: Optional[float] = None, *, want_topp: bool = False,
                   want_importance: bool = False, Y: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, approx_denominator: bool = False):
     """Kernel 2.  Q: [B, H, N, d]; codebook [H, Mt, d]; vsum/counts from assign_aggregate.
     Returns (Y [B, H, N, d] float32, topp [B, H, T, P] int32 or None, importance [B, H, T, M0] or None).
-    ``workspace`` (uint8 device tensor) is allocated here when not given."""
+    ``workspace`` (uint8 device tensor) is allocated here when not given.  ``approx_denominator``
+    selects avq_attention_fwd_approx (importances per 64-parent tile, App. B Eq. 13-14)."""
     B, H, N, d = _shape4(Q, "Q")
     Mt = codebook.shape[1]
     M0 = Mt // (1 + C)
@@ -141,11 +143,13 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
     for name, t in (("vsum", vsum), ("counts", counts)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    rc = _lib.avq_attention_fwd(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
-                                _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(imp),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(Q))
+    fn, name = ((_lib.avq_attention_fwd_approx, "avq_attention_fwd_approx") if approx_denominator
+                else (_lib.avq_attention_fwd, "avq_attention_fwd"))
+    rc = fn(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
+            _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(imp),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(Q))
     if rc != 0:
-        raise AvqError(rc, "avq_attention_fwd")
+        raise AvqError(rc, name)
     return Y, topp, imp
 
 

@@ -72,9 +72,13 @@ size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C, int dtyp
   return avq::attention_workspace_bytes(dtype, d, M0, C, B * H);
 }
 
-int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H,
-                      int N, int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y,
-                      int32_t* topp, float* importance, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int attention_call(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H, int N,
+                   int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
+                   float* importance, void* workspace, size_t workspace_bytes, void* stream, bool approx) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
   if (P < 0 || P > M0 || (C == 0 && P > 0)) return AVQ_ERR_SHAPE;  // no children to refine with
@@ -90,7 +94,26 @@ int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, co
   if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q, importance != nullptr) > (size_t)kMaxLds)
     return AVQ_ERR_UNSUPPORTED;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
-                                        Y, topp, importance, workspace, (hipStream_t)stream));
+                                        Y, topp, importance, workspace, approx, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H,
+                      int N, int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y,
+                      int32_t* topp, float* importance, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
+                        workspace, workspace_bytes, stream, false);
+}
+
+int avq_attention_fwd_approx(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B,
+                             int H, int N, int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y,
+                             int32_t* topp, float* importance, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
+                        workspace, workspace_bytes, stream, true);
 }
 
 const char* avq_status_string(int status) {

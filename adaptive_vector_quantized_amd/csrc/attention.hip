@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
     const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
     int bq, int tiles_per_wg, int wgs_per_bh, float sl2, float* __restrict__ Y, int* __restrict__ topp,
-    float* __restrict__ importance) {
+    float* __restrict__ importance, int approx) {
   using in_t = typename T::in_t;
   using frag_t = typename T::frag_t;
   using pvfrag_t = typename T::pvfrag_t;
@@ -322,7 +322,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sW = sBc + nCH;                                              // [M0p][4] partials per wave
   int* sSel = (int*)(sW + (need_imp ? M0p * 4 : 0));                  // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [2] all parents hold keys; chunk needs masks
-  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 2) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
+  float* sPass = (float*)(sFlag + 2);                                 // [4] keys of the parents of each 64-parent pass
+  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 8) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -373,12 +374,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   if (need_imp)
     for (int i = tid; i < M0p * 4; i += nthreads) sW[i] = 0.0f;
   __syncthreads();
-  for (int c = tid; c < M0p; c += nthreads) {
+  for (int c = tid; c < M0p; c += nthreads) {  // a wave covers the 64 columns of one pass
     const int j = parent_of_col(c);
     const float n = j < M0 ? (float)nb[j] : 0.0f;
     sNp[c] = n;
     sBp[c] = n > 0.0f ? 0.0f : -INFINITY;
     if (j < M0 && !(n > 0.0f)) sFlag[0] = 0;
+    if (approx) {
+      const float tot = wave_sum(n);
+      if (lane == 0) sPass[(c - lane) / 64] = tot;
+    }
   }
   frag_t qf[KS];
   {
@@ -516,12 +521,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             xacc[db] = T::mma_pv((values_lds ? sPV : pvf)[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
         }
       }
+      if constexpr (!parents_lds) {
+        if (approx && need_imp) {
+          // App. B, Eq. 13-14: this pass's importances with the extrapolated
+          // denominator N / N_seen * (the part of Z formed so far), from the
+          // weights still in registers; no second pass over the parents
+          float nseen = 0.0f, ntot = 0.0f;
+          for (int p2 = 0; p2 < nPT; ++p2) {
+            const float c = sPass[p2];
+            ntot += c;
+            if (p2 <= pt) nseen += c;
+          }
+          const float zs = xhalf_sum(zp);
+          const float rz = (qv && nseen > 0.0f) ? nseen / (ntot * zs) : 0.0f;
+          float t[32];
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * rz;
+          rs_half32(t, lane);
+          const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
+          if (j < M0) sW[j * 4 + wave] = t[0] * sNp[j0 + 32 * (ql >> 4) + col_of(ql & 15, hh)];
+        }
+      }
     }
 
     // importance (Eq. 7, Alg. 2 line 8) and top-P (line 9)
     if (need_imp) {
       const float rz = qv ? 1.0f / xhalf_sum(zp) : 0.0f;
-      for (int pt = 0; pt < nPT; ++pt) {
+      for (int pt = 0; pt < ((approx && !parents_lds) ? 0 : nPT); ++pt) {  // (formed in the pass loop)
         const int j0 = pt * 64;
         float t[32];
         if constexpr (parents_lds) {  // one pass (M0 <= 64): its weights are still in registers
@@ -752,7 +780,7 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   b += 2 * ch * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
   if (P > 0 || importance) b += M0p * 4 * 4;           // importance partials
-  b += nw * (size_t)(P > 0 ? P : 1) * 4 + 16; // selections, flag
+  b += nw * (size_t)(P > 0 ? P : 1) * 4 + 32; // selections, flags, keys per pass
   b = (b + 15) & ~(size_t)15;
   b += nw * 32 * kYRow * 4;                   // output staging
   return b;
@@ -779,7 +807,7 @@ int attention_tiles_per_wg(int BH, int N, int bq) {
 template <class T, int D, int W, bool PL>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, hipStream_t st) {
+                                void* ws, bool approx, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
   const size_t sig_bytes = align256((size_t)BH * 4);
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
@@ -804,32 +832,32 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   const float sl2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
                      (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N, M0, C,
-                     P, bq, tpw, per, sl2, Y, topp, importance);
+                     P, bq, tpw, per, sl2, Y, topp, importance, approx ? 1 : 0);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, hipStream_t st) {
+                                void* ws, bool approx, hipStream_t st) {
   const bool pl = M0 <= 64;
   if (C <= 8) {
-    if (pl) return launch_attn_t<T, D, 8, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
-    return launch_attn_t<T, D, 8, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+    if (pl) return launch_attn_t<T, D, 8, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+    return launch_attn_t<T, D, 8, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
   }
-  if (pl) return launch_attn_t<T, D, 16, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
-  return launch_attn_t<T, D, 16, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  if (pl) return launch_attn_t<T, D, 16, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+  return launch_attn_t<T, D, 16, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, hipStream_t st) {
+                            float* importance, void* ws, bool approx, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
-    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
   }
-  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
-  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, st);
+  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
 }
 
 }  // namespace avq

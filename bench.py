@@ -122,6 +122,8 @@ def main():
     ap.add_argument("--P", type=int, default=None)
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated through the timed loop")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--approx-denominator", action="store_true",
+                    help="time avq_attention_fwd_approx (importances per 64-parent tile, App. B Eq. 13-14)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole pass at every refinement budget of the workload (e.g. --workload sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -171,7 +173,7 @@ def main():
         def step(s):
             _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
             _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
-                               Y=s["Y"], workspace=s["ws"])
+                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator)
 
         for i in range(warmup):
             step(sets[i % len(sets)])
@@ -186,7 +188,7 @@ def main():
             _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
             e[1].record(stream)
             _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
-                               Y=s["Y"], workspace=s["ws"])
+                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator)
             e[2].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -240,7 +242,7 @@ def main():
         }
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
     kd = kernels[dom]
-    traffic = load_traffic(dom, cfg.name)
+    traffic = None if args.approx_denominator else load_traffic(dom, cfg.name)  # counters taken on the exact call
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -257,7 +259,8 @@ def main():
         "config": {
             "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N}"
                         + (f" ({cfg.grid}x{cfg.grid} token grid, 8x8-patch clusters)" if cfg.grid else "")
-                        + f" d={cfg.d} M0={cfg.M0} C={cfg.C} P={P} block_q={cfg.block_q}, {cfg.parents} parent occupancy",
+                        + f" d={cfg.d} M0={cfg.M0} C={cfg.C} P={P} block_q={cfg.block_q}, {cfg.parents} parent occupancy"
+                        + (", importance with the approximate tiled denominator" if args.approx_denominator else ""),
             "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "parallelism": "single GPU",
         },
         "roofline": {

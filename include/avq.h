@@ -152,6 +152,25 @@ int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum,
                       float* Y, int32_t* topp, float* importance,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * AVQ attention forward with the approximate tiled denominator of App. B
+ * (Eq. 13-14) for the importances.  The parents are visited in tiles of 64;
+ * after tile J the importances of its parents are formed at once with
+ *   Z~_i(J) = N / N_seen(J) * (sum over the tiles t <= J of sum_{j in t} A_ij n_j),
+ *   w_j = sum_{i in tile} A_ij n_j / Z~_i(J),
+ * where N_seen(J) counts the keys of the parents of tiles 0..J and N all keys
+ * (w_j = 0 while N_seen(J) = 0), so no second pass over the parents is made.
+ * Everything else -- the selection, the refinement and Y with its exact
+ * denominator -- is as in avq_attention_fwd, and so are the arguments,
+ * layouts, workspace and errors.  With M0 <= 64 (one tile) the result equals
+ * avq_attention_fwd's.
+ */
+int avq_attention_fwd_approx(const void* Q, const void* codebook, const float* vsum,
+                             const int32_t* counts, int B, int H, int N, int d, int M0,
+                             int C, int dtype, int P, int block_q, float scale,
+                             float* Y, int32_t* topp, float* importance,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* avq_status_string(int status);
 

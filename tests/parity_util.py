@@ -26,7 +26,8 @@ def to_device(a: np.ndarray, dtype: str, B: int, H: int):
     return t.contiguous().cuda()
 
 
-def run_gpu(data: dict, P: int, want_assign=True, want_topp=True, want_importance=True, bq=None):
+def run_gpu(data: dict, P: int, want_assign=True, want_topp=True, want_importance=True, bq=None,
+            approx=False):
     """Both kernels through the C interface; returns numpy arrays shaped like the oracle's."""
     import torch
     from adaptive_vector_quantized_amd import _lib
@@ -40,7 +41,8 @@ def run_gpu(data: dict, P: int, want_assign=True, want_topp=True, want_importanc
     cb = (cb.to(torch.bfloat16) if cfg.dtype == "bf16" else cb).contiguous().cuda()
     vsum, counts, assign = _lib.assign_aggregate(K, V, cb, cfg.C, want_assign=want_assign)
     Y, topp, imp = _lib.attention_fwd(Q, cb, vsum, counts, cfg.C, P, bq, cfg.scale,
-                                      want_topp=want_topp and P > 0, want_importance=want_importance)
+                                      want_topp=want_topp and P > 0, want_importance=want_importance,
+                                      approx_denominator=approx)
     torch.cuda.synchronize()
     BH = B * H
     out = {

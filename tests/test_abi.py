@@ -21,8 +21,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
-    assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_attention_workspace_size",
-                          "avq_status_string", "avq_version"}
+    assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_attention_fwd_approx",
+                          "avq_attention_workspace_size", "avq_status_string", "avq_version"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -51,14 +51,14 @@ def _assign(L, **kw):
                                   a["dtype"], a["vsum"], a["counts"], a["assign"], None)
 
 
-def _attn(L, **kw):
+def _call_attn(L, fn="avq_attention_fwd", **kw):
     _, p = _buf()
     a = dict(Q=p, cb=p, vsum=p, counts=p, B=1, H=1, N=8, d=64, M0=4, C=2, dtype=1, P=2, bq=64, scale=0.125,
              Y=p, topp=None, imp=None, ws=p, wsb=1 << 30)
     a.update(kw)
-    return L.avq_attention_fwd(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"], a["M0"],
-                               a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"], a["imp"],
-                               a["ws"], a["wsb"], None)
+    return getattr(L, fn)(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"], a["M0"],
+                          a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"], a["imp"],
+                          a["ws"], a["wsb"], None)
 
 
 def test_assign_validation(L):
@@ -82,9 +82,13 @@ def test_assign_validation(L):
     assert _assign(L, H=0, K=None) == 0
 
 
-def test_attention_validation(L):
+@pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx"])
+def test_attention_validation(L, fn):
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 8)
+
+    def _attn(L, **kw):  # both entry points validate the same way
+        return _call_attn(L, fn=fn, **kw)
     assert _attn(L, P=-1) == -2
     assert _attn(L, P=5) == -2
     assert _attn(L, C=0, P=1) == -2  # a flat codebook has no children to refine with

@@ -122,6 +122,42 @@ def test_tiled_parents_d128(dtype):
     _full_check(_data("grid64", d=128, M0=256, H=2, N=2048 + 64 + 5, grid=None, dtype=dtype), 32)
 
 
+@pytest.mark.parametrize("d,M0,P", [(64, 256, 32), (64, 100, 20), (128, 256, 32), (64, 64, 16)])
+def test_approx_denominator(d, M0, P):
+    """App. B (Eq. 13-14) through avq_attention_fwd_approx: importances per
+    64-parent tile with the extrapolated denominator, against the oracle's;
+    top-P sets equal wherever the oracle's P-th and (P+1)-th importances are
+    at least 1e-4 apart (relative) or tie at zero (lower index); the output is
+    the substituted-codebook attention for the selected sets.  With one tile
+    (M0 = 64) the call equals avq_attention_fwd."""
+    data = _data("grid64", d=d, M0=M0, H=2, N=2048 + 64 + 5, grid=None)
+    cfg = data["cfg"]
+    bq = cfg.block_q
+    say(f"[parity] approx denominator d{d} M0{M0} P{P}")
+    g = run_gpu(data, P, approx=True)
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(g["row"], row)
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    assert np.array_equal(g["counts"], counts)
+    w64 = o.importance_tiled_f64(data["Q"], data["codebook"], counts, bq, cfg.scale, 64)
+    werr = np.abs(g["importance"].astype(np.float64) - w64).max()
+    say(f"  importance max|err| = {werr:.3e}")
+    assert werr <= 1e-5 * bq
+    srt = -np.sort(-w64, axis=-1)
+    margin = (srt[..., P - 1] - srt[..., P]) / np.maximum(srt[..., P - 1], 1.0)
+    decisive = (margin >= 1e-4) | ((srt[..., P - 1] == 0.0) & (srt[..., P] == 0.0))
+    sel = o.select(w64.astype(np.float32), P)
+    say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
+    assert decisive.mean() > 0.8
+    assert np.array_equal(g["sel"][decisive], sel[decisive])
+    Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, g["sel"], P, bq, cfg.scale)
+    compare_y(g["Y"], Y, cfg.dtype, f"approx d{d} M0{M0} P{P}")
+    if M0 <= 64:
+        g0 = run_gpu(data, P)
+        assert np.array_equal(g["Y"], g0["Y"]) and np.array_equal(g["sel"], g0["sel"])
+
+
 @pytest.mark.parametrize("M0", [64, 256])
 def test_flat_codebook(M0):
     """C = 0: a flat codebook of M0 codewords, plain VQ attention (P = 0)."""
