@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     float m = -FLT_MAX;
     f32x16 lg[2];
 
-    // parents (Alg. 2 lines 2-7), 64 per pass (the padding rows past M0 have
+    // parents (Alg. 2, the pass over the parent codewords), 64 per pass (the padding rows past M0 have
     // count 0 and logit -inf); parents not held in LDS are read from L2 one
     // 32-row block ahead of their MFMAs
     frag_t pa[parents_lds ? 1 : KS];
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       }
     }
 
-    // importance (Eq. 7, Alg. 2 line 8) and top-P (line 9)
+    // importance (Eq. 7) and top-P (Alg. 2, the parent choice)
     if (need_imp) {
       const float rz = qv ? 1.0f / xhalf_sum(zp) : 0.0f;
       for (int pt = 0; pt < ((approx && !parents_lds) ? 0 : nPT); ++pt) {  // (formed in the pass loop)
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
 
 
-    // children of the selected parents (Alg. 2 lines 10-19), CH rows per chunk
+    // children of the selected parents (Alg. 2, the refinement loop; Eq. 8-9), CH rows per chunk
     if (P > 0) {
       const int* sel = sSel + wave * Pp;
       const float sl2C = sl2 / (float)C;  // Eq. 8's mean folded into the logit scale
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qn[s];
 
-    // Y = x / z (Alg. 2 line 20).  A lane holds 4-float runs of its query's
+    // Y = x / z (Alg. 2, the final normalisation).  A lane holds 4-float runs of its query's
     // row; the wave's output goes through LDS 32 dims at a time.
     const float zt = xhalf_sum(zp);
     const float f = qv ? sig / zt : 0.0f;

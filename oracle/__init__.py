@@ -132,7 +132,7 @@ class Oracle:
         _ok(self.lib.avqo_importance_tiled_f64(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, tile, _p(w)))
         return w
 
-    # Alg. 2 line 9
+    # Alg. 2, the top-P parent choice
     def select(self, w, P: int):
         w = np.ascontiguousarray(w, dtype=np.float32)
         R = int(np.prod(w.shape[:-1]))

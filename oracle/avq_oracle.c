@@ -108,7 +108,7 @@ int avqo_assign(int B, int H, int N, int d, int M0, int C,
     return ORACLE_OK;
 }
 
-/* Eq. 3 with Alg. 1 lines 8 and 16: every key adds its value and a count of one
+/* Eq. 3 with Alg. 1 (the scatter after each assignment level): every key adds its value and a count of one
  * to its parent row (a parent holds its whole cluster); a key that moved also
  * adds them to its child row. */
 int avqo_aggregate(int B, int H, int N, int d, int M0, int C,
@@ -139,7 +139,7 @@ int avqo_aggregate(int B, int H, int N, int d, int M0, int C,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Eq. 7 with Alg. 2 lines 4-8: importance of every parent for every query tile.
+/* Eq. 7 with Alg. 2 (the parent pass and the importance): importance of every parent for every query tile.
  *   s_ij = scale * Q_i . C_j over the parents j,
  *   m_i  = max of s_ij over the parents with n_j > 0 (Eq. 18),
  *   A_ij = exp(s_ij - m_i), set to zero where n_j = 0 (Sec. D),
@@ -183,7 +183,7 @@ int avqo_importance(int B, int H, int N, int d, int M0, int C,
     return ORACLE_OK;
 }
 
-/* Alg. 2 line 9: the P parents of largest importance.  Equal importances are
+/* Alg. 2, the parent choice: the P parents of largest importance.  Equal importances are
  * ordered by the lower parent index.  The chosen set is written ascending.
  * w: [R][M0] (R = BH*T rows), sel: [R][P]. */
 int avqo_select(int64_t R, int M0, int P, const float* w, int32_t* sel) {
@@ -244,7 +244,7 @@ int avqo_attention_alg2(int B, int H, int N, int d, int M0, int C,
             const int t = i / bq;
             const int32_t* S = sel + ((int64_t)bh * T + t) * P;
             const double* q = Q + ((int64_t)bh * N + i) * d;
-            /* lines 4-7 */
+            /* the parent pass */
             double m = -INFINITY;
             for (int j = 0; j < M0; ++j) {
                 s[j] = scale * dotd(q, cbh + (int64_t)j * d, d);
@@ -257,7 +257,7 @@ int avqo_attention_alg2(int B, int H, int N, int d, int M0, int C,
                 for (int u = 0; u < d; ++u) x[u] += A * vs[(int64_t)j * d + u];
                 z += A * n[j];
             }
-            /* lines 10-19 */
+            /* the refinement over the selected parents' children */
             for (int k = 0; k < P; ++k) {
                 const int64_t c0 = M0 + (int64_t)S[k] * C;
                 double mnew = m;

@@ -63,8 +63,8 @@ def pin_assign_ties(lib):
     """Ties, on small integer data whose squared distances are exact in any
     precision: equal parent distances go to the lower parent index; equal
     child distances to the lower child; a child exactly as close as the parent
-    does not take the key (Alg. 1: arg min on line 7, strict comparisons on
-    lines 14 and 16)."""
+    does not take the key (Alg. 1: arg min over the parents, strict
+    comparisons in the child updates)."""
     d, M0, C = 2, 3, 2
     cb = np.zeros((1, M0 * (1 + C), d))
     cb[0, :M0] = [[0, 0], [4, 0], [0, 40]]
@@ -171,7 +171,7 @@ def pin_importance_properties(lib):
 
 
 def pin_select(lib):
-    """Alg. 2 line 9: the P largest importances, ties to the lower index,
+    """Alg. 2, the parent choice: the P largest importances, ties to the lower index,
     written ascending; P = M0 selects every parent, P = 0 none."""
     o = _O(lib, 1, 1, 1, 1, 6, 1)
     w = np.array([[0.5, 2.0, 2.0, 0.1, 3.0, 0.5]], np.float32)
