@@ -41,6 +41,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (lib.avq_attention_fwd, lib.avq_attention_fwd_approx):
         f.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P, ctypes.c_size_t, P]
         f.restype = i32
+    lib.avq_attention_fwd_ordered.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, i32, P, P, P, P,
+                                                                      ctypes.c_size_t, P]
+    lib.avq_attention_fwd_ordered.restype = i32
     lib.avq_attention_workspace_size.argtypes = [i32] * 6
     lib.avq_attention_workspace_size.restype = ctypes.c_size_t
     lib.avq_status_string.argtypes = [i32]
@@ -121,11 +124,15 @@ def workspace_size(B: int, H: int, d: int, M0: int, C: int, dtype: torch.dtype) 
 def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, counts: torch.Tensor, C: int, P: int,
                   block_q: int, scale: Optional[float] = None, *, want_topp: bool = False,
                   want_importance: bool = False, Y: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, approx_denominator: bool = False):
+                  workspace: Optional[torch.Tensor] = None, approx_denominator: bool = False,
+                  query_order: Optional[torch.Tensor] = None):
     """Kernel 2.  Q: [B, H, N, d]; codebook [H, Mt, d]; vsum/counts from assign_aggregate.
     Returns (Y [B, H, N, d] float32, topp [B, H, T, P] int32 or None, importance [B, H, T, M0] or None).
     ``workspace`` (uint8 device tensor) is allocated here when not given.  ``approx_denominator``
-    selects avq_attention_fwd_approx (importances per 64-parent tile, App. B Eq. 13-14)."""
+    selects avq_attention_fwd_approx (importances per 64-parent tile, App. B Eq. 13-14).
+    ``query_order`` (int32 [N] device tensor, a permutation of the token rows, e.g.
+    ``gilbert.query_order``) selects avq_attention_fwd_ordered: tile t holds the
+    queries of rows query_order[t*block_q ...]; Y stays in the row order of Q."""
     B, H, N, d = _shape4(Q, "Q")
     Mt = codebook.shape[1]
     M0 = Mt // (1 + C)
@@ -143,11 +150,22 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
     for name, t in (("vsum", vsum), ("counts", counts)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    fn, name = ((_lib.avq_attention_fwd_approx, "avq_attention_fwd_approx") if approx_denominator
-                else (_lib.avq_attention_fwd, "avq_attention_fwd"))
-    rc = fn(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
-            _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(imp),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(Q))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if query_order is not None:
+        if (query_order.dtype != torch.int32 or query_order.dim() != 1 or query_order.numel() != N
+                or not query_order.is_contiguous() or query_order.device != dev):
+            raise ValueError("query_order must be a contiguous int32 [N] tensor on the device of Q")
+        name = "avq_attention_fwd_ordered"
+        rc = _lib.avq_attention_fwd_ordered(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
+                                            _dtype_code(Q), P, block_q, float(scale), _ptr(query_order),
+                                            1 if approx_denominator else 0, _ptr(Y), _ptr(topp), _ptr(imp),
+                                            _ptr(workspace), ws_bytes, _stream(Q))
+    else:
+        fn, name = ((_lib.avq_attention_fwd_approx, "avq_attention_fwd_approx") if approx_denominator
+                    else (_lib.avq_attention_fwd, "avq_attention_fwd"))
+        rc = fn(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
+                _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(imp),
+                _ptr(workspace), ws_bytes, _stream(Q))
     if rc != 0:
         raise AvqError(rc, name)
     return Y, topp, imp

@@ -78,7 +78,8 @@ namespace {
 
 int attention_call(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H, int N,
                    int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
-                   float* importance, void* workspace, size_t workspace_bytes, void* stream, bool approx) {
+                   float* importance, void* workspace, size_t workspace_bytes, void* stream, bool approx,
+                   const int32_t* order, bool ordered) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
   if (P < 0 || P > M0 || (C == 0 && P > 0)) return AVQ_ERR_SHAPE;  // no children to refine with
@@ -86,15 +87,16 @@ int attention_call(const void* Q, const void* codebook, const float* vsum, const
   if (!isfinite(scale) || !(scale > 0.0f)) return AVQ_ERR_SHAPE;
   const int64_t BH = (int64_t)B * H;
   if (BH == 0 || N == 0) return AVQ_OK;
-  if (!Q || !codebook || !vsum || !counts || !Y || !workspace) return AVQ_ERR_NULL;
+  if (!Q || !codebook || !vsum || !counts || !Y || !workspace || (ordered && !order)) return AVQ_ERR_NULL;
   if (!aligned16(Q) || !aligned16(codebook) || !aligned16(vsum) || !aligned16(counts) || !aligned16(Y) ||
-      !aligned16(workspace) || (topp && !aligned16(topp)) || (importance && !aligned16(importance)))
+      !aligned16(workspace) || (topp && !aligned16(topp)) || (importance && !aligned16(importance)) ||
+      ((uintptr_t)order & 3u) != 0)
     return AVQ_ERR_ALIGN;
   if (workspace_bytes < avq::attention_workspace_bytes(dtype, d, M0, C, (int)BH)) return AVQ_ERR_WORKSPACE;
   if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q, importance != nullptr) > (size_t)kMaxLds)
     return AVQ_ERR_UNSUPPORTED;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
-                                        Y, topp, importance, workspace, approx, (hipStream_t)stream));
+                                        Y, topp, importance, workspace, approx, order, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -105,7 +107,7 @@ int avq_attention_fwd(const void* Q, const void* codebook, const float* vsum, co
                       int N, int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y,
                       int32_t* topp, float* importance, void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
-                        workspace, workspace_bytes, stream, false);
+                        workspace, workspace_bytes, stream, false, nullptr, false);
 }
 
 int avq_attention_fwd_approx(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B,
@@ -113,7 +115,15 @@ int avq_attention_fwd_approx(const void* Q, const void* codebook, const float* v
                              int32_t* topp, float* importance, void* workspace, size_t workspace_bytes,
                              void* stream) {
   return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
-                        workspace, workspace_bytes, stream, true);
+                        workspace, workspace_bytes, stream, true, nullptr, false);
+}
+
+int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B,
+                              int H, int N, int d, int M0, int C, int dtype, int P, int block_q, float scale,
+                              const int32_t* query_order, int approx_denominator, float* Y, int32_t* topp,
+                              float* importance, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
+                        workspace, workspace_bytes, stream, approx_denominator != 0, query_order, true);
 }
 
 const char* avq_status_string(int status) {

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
     const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
     int bq, int tiles_per_wg, int wgs_per_bh, float sl2, float* __restrict__ Y, int* __restrict__ topp,
-    float* __restrict__ importance, int approx) {
+    float* __restrict__ importance, int approx, const int* __restrict__ order) {
   using in_t = typename T::in_t;
   using frag_t = typename T::frag_t;
   using pvfrag_t = typename T::pvfrag_t;
@@ -385,10 +385,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       if (lane == 0) sPass[(c - lane) / 64] = tot;
     }
   }
+  // Token row of the query at tile position pos, -1 for none: the position
+  // itself, or with a query order the row it names (a name outside [0, N)
+  // makes the position empty, like the positions past N of the last tile).
+  // The order entries are fetched one tile ahead of the query loads that use
+  // them, so that those loads never wait for them.
+  auto order_at = [&](int pos) -> int { return (order != nullptr && pos < N) ? order[pos] : pos; };
+  auto query_row = [&](int pos, int entry) -> int {
+    if (pos >= N) return -1;
+    if (order == nullptr) return pos;
+    return (entry >= 0 && entry < N) ? entry : -1;
+  };
+  const int qpos0 = tile0 * bq + wave * 32 + ql;
   frag_t qf[KS];
+  int qrow = query_row(qpos0, order_at(qpos0));
+  int entry_n = order_at(qpos0 + bq);  // the order entry of this lane's query in the next tile
   {
-    const int qi = tile0 * bq + wave * 32 + ql;
-    const in_t* qp = Qb + (int64_t)(qi < N ? qi : N - 1) * D + E * hh;
+    const in_t* qp = Qb + (int64_t)(qrow >= 0 ? qrow : 0) * D + E * hh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = *(const frag_t*)(qp + s * 2 * E);
   }
@@ -401,10 +414,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // as streaming (non-temporal) stores: the output is never read back here,
   // and keeping it out of L2 leaves L2 to the codewords and value fragments.
   float* yw = sY + wave * 32 * kYRow;
-  auto store_rows = [&](int q0, int db) {
+  auto store_rows = [&](int q0, int db, int row) {
     __builtin_amdgcn_wave_barrier();
     const int r0 = lane >> 3, c4 = (lane & 7) * 4;
     const float* src = yw + r0 * kYRow + c4;
+    if (order != nullptr) {
+      // rows scattered by the query order: each 8-lane group still writes one
+      // whole 128-byte segment of its row; lane r of the wave holds the row of
+      // the wave's r-th query
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = __shfl(row, r0 + 8 * k);
+        if (r >= 0)
+          __builtin_nontemporal_store(*(const f32x4*)(src + 8 * k * kYRow), (f32x4*)(Yb + (int64_t)r * D + db * 32 + c4));
+      }
+      return;
+    }
     float* dst = Yb + (int64_t)(q0 + r0) * D + db * 32 + c4;
     if (q0 + 32 <= N) {
 #pragma unroll
@@ -419,17 +444,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   // ---- query tiles ------------------------------------------------------------
   for (int tile = tile0; tile < tile1; ++tile) {
-    const int qi = tile * bq + wave * 32 + ql;
-    const bool qv = qi < N;
+    const bool qv = qrow >= 0;
     // the next tile's queries, a whole tile ahead of their use (d = 64; at
     // d = 128 they are loaded at the end of the tile, saving registers)
     constexpr bool kEarlyQ = D == 64;
     frag_t qn[KS];
+    int qrow_n = -1;
     auto load_next_q = [&]() {
-      const int qn_i = (tile + 1) * bq + wave * 32 + ql;
-      const in_t* qp = Qb + (int64_t)(qn_i < N ? qn_i : N - 1) * D + E * hh;
+      const int pos = (tile + 1) * bq + wave * 32 + ql;
+      qrow_n = query_row(pos, entry_n);
+      const in_t* qp = Qb + (int64_t)(qrow_n >= 0 ? qrow_n : 0) * D + E * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) qn[s] = *(const frag_t*)(qp + s * 2 * E);
+      entry_n = order_at(pos + bq);
     };
     if constexpr (kEarlyQ) load_next_q();
 
@@ -748,6 +775,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if constexpr (!kEarlyQ) load_next_q();
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = qn[s];
+    const int qrow_t = qrow;
+    qrow = qrow_n;
 
     // Y = x / z (Alg. 2, the final normalisation).  A lane holds 4-float runs of its query's
     // row; the wave's output goes through LDS 32 dims at a time.
@@ -763,7 +792,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         const f32x4 o = {a[4 * i] * f, a[4 * i + 1] * f, a[4 * i + 2] * f, a[4 * i + 3] * f};
         *(f32x4*)(yw + ql * kYRow + 8 * i + 4 * hh) = o;
       }
-      store_rows(q0, db);
+      store_rows(q0, db, qrow_t);
     }
   }
 }
@@ -807,7 +836,7 @@ int attention_tiles_per_wg(int BH, int N, int bq) {
 template <class T, int D, int W, bool PL>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, hipStream_t st) {
+                                void* ws, bool approx, const int* order, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
   const size_t sig_bytes = align256((size_t)BH * 4);
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
@@ -832,32 +861,32 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   const float sl2 = scale * 1.4426950408889634f;
   hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
                      (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N, M0, C,
-                     P, bq, tpw, per, sl2, Y, topp, importance, approx ? 1 : 0);
+                     P, bq, tpw, per, sl2, Y, topp, importance, approx ? 1 : 0, order);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, hipStream_t st) {
+                                void* ws, bool approx, const int* order, hipStream_t st) {
   const bool pl = M0 <= 64;
   if (C <= 8) {
-    if (pl) return launch_attn_t<T, D, 8, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
-    return launch_attn_t<T, D, 8, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+    if (pl) return launch_attn_t<T, D, 8, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+    return launch_attn_t<T, D, 8, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
   }
-  if (pl) return launch_attn_t<T, D, 16, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
-  return launch_attn_t<T, D, 16, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+  if (pl) return launch_attn_t<T, D, 16, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+  return launch_attn_t<T, D, 16, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, bool approx, hipStream_t st) {
+                            float* importance, void* ws, bool approx, const int* order, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
-    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
   }
-  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
-  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, st);
+  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
 }
 
 }  // namespace avq

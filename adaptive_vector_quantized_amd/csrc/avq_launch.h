@@ -31,6 +31,6 @@ hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH);
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, bool approx, hipStream_t st);
+                            float* importance, void* ws, bool approx, const int* order, hipStream_t st);
 
 }  // namespace avq

@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--approx-denominator", action="store_true",
                     help="time avq_attention_fwd_approx (importances per 64-parent tile, App. B Eq. 13-14)")
+    ap.add_argument("--query-order", choices=("raster", "gilbert"), default="raster",
+                    help="query tiles in row-major order, or along the Gilbert curve of the token grid "
+                         "(avq_attention_fwd_ordered)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole pass at every refinement budget of the workload (e.g. --workload sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -137,7 +140,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from adaptive_vector_quantized_amd import _lib, gen
+    from adaptive_vector_quantized_amd import _lib, gen, gilbert
 
     cfg = gen.CONFIGS[args.workload]
     P = cfg.P if args.P is None else args.P
@@ -166,6 +169,11 @@ def main():
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
+    qorder = None
+    if args.query_order == "gilbert":
+        if cfg.grid is None:
+            raise SystemExit("--query-order gilbert needs a workload on a token grid")
+        qorder = torch.from_numpy(gilbert.query_order(cfg.grid, cfg.grid)).to(dev)
 
     def timed(P, steps, warmup):
         """Warm up, then time `steps` whole passes at refinement budget P: wall
@@ -173,7 +181,8 @@ def main():
         def step(s):
             _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
             _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
-                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator)
+                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator,
+                               query_order=qorder)
 
         for i in range(warmup):
             step(sets[i % len(sets)])
@@ -188,7 +197,8 @@ def main():
             _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
             e[1].record(stream)
             _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
-                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator)
+                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator,
+                               query_order=qorder)
             e[2].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -242,7 +252,8 @@ def main():
         }
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
     kd = kernels[dom]
-    traffic = None if args.approx_denominator else load_traffic(dom, cfg.name)  # counters taken on the exact call
+    # counters taken on the exact call in row-major order
+    traffic = None if (args.approx_denominator or qorder is not None) else load_traffic(dom, cfg.name)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -260,7 +271,8 @@ def main():
             "workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N}"
                         + (f" ({cfg.grid}x{cfg.grid} token grid, 8x8-patch clusters)" if cfg.grid else "")
                         + f" d={cfg.d} M0={cfg.M0} C={cfg.C} P={P} block_q={cfg.block_q}, {cfg.parents} parent occupancy"
-                        + (", importance with the approximate tiled denominator" if args.approx_denominator else ""),
+                        + (", importance with the approximate tiled denominator" if args.approx_denominator else "")
+                        + (", query tiles along the Gilbert curve" if qorder is not None else ""),
             "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "parallelism": "single GPU",
         },
         "roofline": {

@@ -171,6 +171,39 @@ int avq_attention_fwd_approx(const void* Q, const void* codebook, const float* v
                              float* Y, int32_t* topp, float* importance,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * AVQ attention forward with the query tiles taken in a given token order
+ * (Sec. 4.3 and Fig. 3: the queries of an image are put in the order of a
+ * Gilbert space-filling curve, so that each tile of block_q consecutive
+ * positions along the curve is a compact 2-D region and shares one parent
+ * selection; App. H, Tab. 8 compares curve, raster and random orders).
+ *
+ * Tile t holds the queries of the rows query_order[t*block_q + i],
+ * 0 <= i < block_q (the last tile may be partial), and the output of each
+ * query goes to its own row of Y, so Y is in the row order of Q whatever the
+ * query order.  With query_order[i] = i this is avq_attention_fwd (or
+ * avq_attention_fwd_approx when approx_denominator is nonzero); topp and
+ * importance are indexed by tile, in the given order.
+ *
+ *   query_order  in  [N] int32 device array, 4-byte aligned, shared by every
+ *                (batch, head): a permutation of 0 .. N-1.  An entry outside
+ *                [0, N) makes its position empty: it adds nothing to its
+ *                tile's importances and no row is written for it.  A row
+ *                named twice is written twice (which value stays is
+ *                unspecified); a row never named is not written.
+ *   approx_denominator  nonzero: the importances of avq_attention_fwd_approx
+ *
+ * Every other argument, layout, the workspace and the errors are those of
+ * avq_attention_fwd; a NULL query_order is AVQ_ERR_NULL (when B*H and N are
+ * not zero).
+ */
+int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* vsum,
+                              const int32_t* counts, int B, int H, int N, int d, int M0,
+                              int C, int dtype, int P, int block_q, float scale,
+                              const int32_t* query_order, int approx_denominator,
+                              float* Y, int32_t* topp, float* importance,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* avq_status_string(int status);
 

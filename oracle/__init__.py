@@ -184,6 +184,36 @@ class Oracle:
         _ok(self.lib.avqo_tile_margins(*self.dims, _p(Q), _p(cb), _p(counts), bq, P, scale, _p(out)))
         return out
 
+    # Sec. 4.3 and Fig. 3: query tiles taken along a token order
+    def ordered(self, Q, order):
+        """The queries in tile order: tile t holds the queries of rows
+        order[t*bq ...].  Returns (an Oracle over the ordered queries, the
+        ordered queries [BH, n, d], the rows they came from [n]).  Entries of
+        ``order`` outside [0, N) are empty positions and must all follow the
+        valid ones (the valid positions then tile like a shorter query array);
+        a row named twice is rejected.  The per-tile steps (importance,
+        selection, output) take the ordered queries unchanged: a tile is a set
+        of queries, whatever rows they sit on."""
+        order = np.asarray(order, dtype=np.int64).reshape(-1)
+        if order.size != self.N:
+            raise ValueError("the order names one row per position (N entries)")
+        valid = (order >= 0) & (order < self.N)
+        n = int(valid.sum())
+        if not valid[:n].all():
+            raise ValueError("empty positions must follow the valid ones")
+        rows = order[:n]
+        if np.unique(rows).size != n:
+            raise ValueError("a row is named twice")
+        Qo = np.asarray(Q)[:, rows]
+        return Oracle(self.B, self.H, n, self.d, self.M0, self.C, lib=self.lib), Qo, rows
+
+    def scatter_rows(self, Yo, rows):
+        """Outputs in tile order back to the rows of their queries; rows that
+        no position names are NaN."""
+        Y = np.full((self.B * self.H, self.N, self.d), np.nan)
+        Y[:, rows] = Yo
+        return Y
+
     # the whole forward pass in one call: discrete results + all three output forms
     def forward(self, Q, K, V, codebook, P: int, bq: int, scale: float, forms=("substituted",)):
         parent, row = self.assign(K, codebook)

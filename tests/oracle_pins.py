@@ -430,6 +430,104 @@ def pin_importance_tiled(lib):
     np.testing.assert_allclose(o.importance_tiled_f64(Q, cb, counts, bq, scale, M0), exact, rtol=1e-12, atol=1e-15)
 
 
+# ---------------------------------------------------------------- query order
+def _run_ordered(o, data, counts, vsum, order, P, bq, scale):
+    """Importance (float and double), selection and output with the query tiles
+    taken along ``order``, through the oracle's ordering step."""
+    oq, Qo, rows = o.ordered(data["Q"], order)
+    cb = data["codebook"]
+    w = oq.importance(Qo, cb, counts, bq, scale)
+    w64 = oq.importance_f64(Qo, cb, counts, bq, scale)
+    sel = oq.select(w, P)
+    Y = o.scatter_rows(oq.attention_substituted(Qo, cb, vsum, counts, sel, P, bq, scale), rows)
+    return w64, sel, Y
+
+
+def _ordered_setup(lib, seed, N=96, M0=6, C=3):
+    cfg, data = _small_case(seed, N=N, d=8, M0=M0, C=C)
+    o = _O(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C)
+    parent, row = o.assign(data["K"], data["codebook"])
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    return cfg, data, o, vsum, counts
+
+
+def pin_order_tile_relabel(lib):
+    """Sec. 4.3: a tile is a set of queries.  An order that moves whole row-major
+    tiles (a 3-cycle) and reverses or rotates the queries inside some tiles
+    gives every query the same tile-mates, so the output rows are those of the
+    row-major order, and tile t's importances and selection are those of the
+    row-major tile whose queries it holds."""
+    cfg, data, o, vsum, counts = _ordered_setup(lib, 41)
+    bq, P = cfg.block_q, 2
+    T = cfg.N // bq
+    src = [1, 2, 0] + list(range(3, T))       # tile t holds the queries of row-major tile src[t]
+    order = np.empty(cfg.N, np.int64)
+    for t in range(T):
+        r = np.arange(src[t] * bq, (src[t] + 1) * bq)
+        if t in (0, 2):
+            r = r[::-1]
+        elif t == 4:
+            r = np.roll(r, 5)
+        order[t * bq:(t + 1) * bq] = r
+    w_ref = o.importance_f64(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    sel_ref = o.select(o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale), P)
+    Y_ref = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel_ref, P, bq, cfg.scale)
+    w, sel, Y = _run_ordered(o, data, counts, vsum, order, P, bq, cfg.scale)
+    np.testing.assert_allclose(w, w_ref[:, src], rtol=1e-12, atol=1e-15)
+    assert np.array_equal(sel, sel_ref[:, src])
+    np.testing.assert_allclose(Y, Y_ref, rtol=1e-12, atol=1e-14)
+
+
+def pin_order_homogeneous_tiles(lib):
+    """An order that gathers equal queries into tiles: rows alternate between
+    two query vectors q_a and q_b (aligned with two different parents), and
+    the order lists the even rows, then the odd ones, so every tile holds one
+    vector only.  Each output row then equals the output of a tile made of
+    copies of its query (the row-major order mixes the two in every tile and
+    gives a different result)."""
+    cfg, data, o, vsum, counts = _ordered_setup(lib, 43, N=64)
+    bq, P = cfg.block_q, 1
+    cb = data["codebook"]
+    qa, qb = 6.0 * cb[:, 0], 6.0 * cb[:, 3]   # per head [H, d]
+    Q = np.empty((cfg.BH, cfg.N, cfg.d))
+    Q[:, 0::2] = qa[:, None]
+    Q[:, 1::2] = qb[:, None]
+    order = np.concatenate([np.arange(0, cfg.N, 2), np.arange(1, cfg.N, 2)])
+    _, _, Y = _run_ordered(o, dict(data, Q=Q), counts, vsum, order, P, bq, cfg.scale)
+    for q, rows in ((qa, slice(0, None, 2)), (qb, slice(1, None, 2))):
+        Qh = np.repeat(q[:, None], bq, axis=1)      # one tile of copies
+        o1 = _O(lib, cfg.B, cfg.H, bq, cfg.d, cfg.M0, cfg.C)
+        sel = o1.select(o1.importance(Qh, cb, counts, bq, cfg.scale), P)
+        y = o1.attention_substituted(Qh, cb, vsum, counts, sel, P, bq, cfg.scale)[:, :1]
+        np.testing.assert_allclose(Y[:, rows], np.broadcast_to(y, Y[:, rows].shape), rtol=1e-12, atol=1e-14)
+    sel_rm = o.select(o.importance(Q, cb, counts, bq, cfg.scale), P)
+    Y_rm = o.attention_substituted(Q, cb, vsum, counts, sel_rm, P, bq, cfg.scale)
+    assert np.abs(Y_rm - Y).max() > 1e-3
+
+
+def pin_order_trailing_empty(lib):
+    """Positions that name no row (outside [0, N)) at the end of the order:
+    the tiles before them are unchanged, the rows they would have named are
+    not written, and the importances of the last tile sum to its number of
+    named queries (Eq. 7: each query's normalised weights sum to one)."""
+    cfg, data, o, vsum, counts = _ordered_setup(lib, 47)
+    bq, P = cfg.block_q, 2
+    order = np.random.default_rng(3).permutation(cfg.N)
+    w_full, sel_full, Y_full = _run_ordered(o, data, counts, vsum, order, P, bq, cfg.scale)
+    cut = order.copy()
+    dropped = cut[-5:].copy()
+    cut[-5:] = -1
+    cut[-2] = cfg.N + 3
+    w, sel, Y = _run_ordered(o, data, counts, vsum, cut, P, bq, cfg.scale)
+    T = cfg.N // bq
+    np.testing.assert_allclose(w[:, :T - 1], w_full[:, :T - 1], rtol=1e-12, atol=1e-15)
+    assert np.array_equal(sel[:, :T - 1], sel_full[:, :T - 1])
+    kept = order[:(T - 1) * bq]
+    np.testing.assert_allclose(Y[:, kept], Y_full[:, kept], rtol=1e-12, atol=1e-14)
+    assert np.isnan(Y[:, dropped]).all() and not np.isnan(Y[:, cut[:-5]]).any()
+    np.testing.assert_allclose(w[:, T - 1].sum(-1), bq - 5, rtol=1e-12)
+
+
 PINS = {
     "assign_ground_truth": pin_assign_ground_truth,
     "assign_copies": pin_assign_copies,
@@ -448,4 +546,7 @@ PINS = {
     "margins": pin_margins,
     "flat_codebook": pin_flat_codebook,
     "importance_tiled": pin_importance_tiled,
+    "order_tile_relabel": pin_order_tile_relabel,
+    "order_homogeneous_tiles": pin_order_homogeneous_tiles,
+    "order_trailing_empty": pin_order_trailing_empty,
 }

@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
     assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_attention_fwd_approx",
-                          "avq_attention_workspace_size", "avq_status_string", "avq_version"}
+                          "avq_attention_fwd_ordered", "avq_attention_workspace_size", "avq_status_string",
+                          "avq_version"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -54,8 +55,12 @@ def _assign(L, **kw):
 def _call_attn(L, fn="avq_attention_fwd", **kw):
     _, p = _buf()
     a = dict(Q=p, cb=p, vsum=p, counts=p, B=1, H=1, N=8, d=64, M0=4, C=2, dtype=1, P=2, bq=64, scale=0.125,
-             Y=p, topp=None, imp=None, ws=p, wsb=1 << 30)
+             Y=p, topp=None, imp=None, ws=p, wsb=1 << 30, order=p, approx=0)
     a.update(kw)
+    if fn == "avq_attention_fwd_ordered":
+        return L.avq_attention_fwd_ordered(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"],
+                                           a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["order"],
+                                           a["approx"], a["Y"], a["topp"], a["imp"], a["ws"], a["wsb"], None)
     return getattr(L, fn)(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"], a["M0"],
                           a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"], a["imp"],
                           a["ws"], a["wsb"], None)
@@ -82,7 +87,7 @@ def test_assign_validation(L):
     assert _assign(L, H=0, K=None) == 0
 
 
-@pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx"])
+@pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx", "avq_attention_fwd_ordered"])
 def test_attention_validation(L, fn):
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 8)
@@ -112,6 +117,17 @@ def test_attention_validation(L, fn):
     assert L.avq_attention_workspace_size(1, 1, 96, 4, 2, 1) == 0   # invalid sizes
     assert _attn(L, N=0) == 0         # no queries: nothing to do
     assert _attn(L, B=0, Q=None) == 0
+
+
+def test_ordered_validation(L):
+    _, p = _buf()
+
+    def _attn(**kw):
+        return _call_attn(L, fn="avq_attention_fwd_ordered", **kw)
+    assert _attn(order=None) == -1                          # the order is required
+    assert _attn(order=ctypes.c_void_p(p.value + 2)) == -4  # int32 entries: 4-byte aligned
+    assert _attn(order=ctypes.c_void_p(p.value + 4), approx=1, P=9) == -2  # the rest as avq_attention_fwd
+    assert _attn(N=0, order=None) == 0                      # no queries: nothing to do
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

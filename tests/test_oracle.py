@@ -3,6 +3,7 @@ and planted mistakes in copies of the oracle that some pin must catch."""
 import os
 import subprocess
 
+import numpy as np
 import pytest
 
 import oracle
@@ -64,4 +65,48 @@ def test_mutant_is_caught(what, old, new, tmp_path):
             pin(lib)
         except AssertionError:
             failed.append(name)
+    assert failed, f"no pin catches: {what}"
+
+
+# planted mistakes in the ordering step of the oracle (Python), each of which
+# some pin must catch
+_real_ordered = oracle.Oracle.ordered
+
+
+def _gather_by_inverse(self, Q, order):
+    order = np.asarray(order)
+    if np.array_equal(np.sort(order), np.arange(order.size)):
+        order = np.argsort(order)
+    return _real_ordered(self, Q, order)
+
+
+def _left_in_tile_order(self, Yo, rows):
+    Y = np.full((self.B * self.H, self.N, self.d), np.nan)
+    Y[:, :len(rows)] = Yo
+    return Y
+
+
+def _empty_reads_row_zero(self, Q, order):
+    order = np.asarray(order, np.int64)
+    rows = np.where((order >= 0) & (order < self.N), order, 0)
+    return oracle.Oracle(self.B, self.H, self.N, self.d, self.M0, self.C, lib=self.lib), np.asarray(Q)[:, rows], rows
+
+
+ORDER_MUTANTS = [
+    ("queries gathered by the inverse order", "ordered", _gather_by_inverse),
+    ("outputs left in tile order", "scatter_rows", _left_in_tile_order),
+    ("empty positions read row 0", "ordered", _empty_reads_row_zero),
+]
+
+
+@pytest.mark.parametrize("what,attr,fn", ORDER_MUTANTS, ids=[m[0] for m in ORDER_MUTANTS])
+def test_order_mutant_is_caught(what, attr, fn, oracle_lib, monkeypatch):
+    monkeypatch.setattr(oracle.Oracle, attr, fn)
+    failed = []
+    for name, pin in PINS.items():
+        if name.startswith("order_"):
+            try:
+                pin(oracle_lib)
+            except AssertionError:
+                failed.append(name)
     assert failed, f"no pin catches: {what}"

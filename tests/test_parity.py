@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from adaptive_vector_quantized_amd import gen
+from adaptive_vector_quantized_amd import gen, gilbert
 from parity_util import check_vsum, compare_y, run_gpu, say, sub_problem
 
 pytestmark = pytest.mark.gpu
@@ -158,6 +158,104 @@ def test_approx_denominator(d, M0, P):
         assert np.array_equal(g["Y"], g0["Y"]) and np.array_equal(g["sel"], g0["sel"])
 
 
+def _place_along(data, order):
+    """The generator's queries put on the rows the order names: position i of
+    the order holds generated query i, so the tiles taken along the order are
+    the generated tiles, drawn clear of top-P ties."""
+    Q = np.full_like(data["Q"], np.nan)
+    valid = (order >= 0) & (order < data["cfg"].N)
+    Q[:, order[valid]] = data["Q"][:, :int(valid.sum())]
+    unnamed = np.isnan(Q[:, :, 0])
+    Q[unnamed] = 0.0
+    return dict(data, Q=Q)
+
+
+def _ordered_check(data, P, order, approx=False, nan_fill=False):
+    """avq_attention_fwd_ordered against the oracle with its queries put in
+    tile order: assignments and counts exact, importances within 1e-5 * |tile|,
+    top-P equal wherever the P-th and (P+1)-th importances are 1e-4 apart
+    (relative), and Y for the chosen sets at its own rows; rows no position
+    names are left as they were."""
+    cfg = data["cfg"]
+    bq = cfg.block_q
+    say(f"[parity] ordered {cfg.name} B{cfg.B} H{cfg.H} N{cfg.N} d{cfg.d} M0{cfg.M0} P{P} bq{bq} {cfg.dtype}"
+        f" approx={approx}")
+    g = run_gpu(data, P, approx=approx, order=order, y_fill=np.nan if nan_fill else None)
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(g["row"], row)
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    assert np.array_equal(g["counts"], counts)
+    oq, Qo, rows = o.ordered(data["Q"], order)
+    cb = data["codebook"]
+    if approx:
+        w64 = oq.importance_tiled_f64(Qo, cb, counts, bq, cfg.scale, 64)
+        w = w64.astype(np.float32)
+    else:
+        w = oq.importance(Qo, cb, counts, bq, cfg.scale)
+        w64 = oq.importance_f64(Qo, cb, counts, bq, cfg.scale)
+    T = w64.shape[1]
+    werr = np.abs(g["importance"][:, :T].astype(np.float64) - w64).max()
+    say(f"  importance max|err| = {werr:.3e}")
+    assert werr <= 1e-5 * bq
+    if P > 0:
+        srt = -np.sort(-w64, axis=-1)
+        margin = (srt[..., P - 1] - srt[..., P]) / np.maximum(srt[..., P - 1], 1.0)
+        decisive = (margin >= 1e-4) | ((srt[..., P - 1] == 0.0) & (srt[..., P] == 0.0))
+        sel = oq.select(w, P)
+        say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
+        assert decisive.mean() > 0.9
+        assert np.array_equal(g["sel"][:, :T][decisive], sel[decisive])
+        sel = g["sel"][:, :T]
+    else:
+        sel = np.zeros((cfg.BH, T, 0), np.int32)
+    Y = o.scatter_rows(oq.attention_substituted(Qo, cb, vsum, counts, sel, P, bq, cfg.scale), rows)
+    named = np.zeros(cfg.N, bool)
+    named[rows] = True
+    compare_y(g["Y"][:, named], Y[:, named], cfg.dtype, f"ordered {cfg.name} P={P}")
+    if nan_fill:
+        assert np.isnan(g["Y"][:, ~named]).all(), "a row no position names was written"
+
+
+@pytest.mark.parametrize("approx", [False, True])
+def test_ordered_gilbert_grid64(approx):
+    """Sec. 4.3 and Fig. 3: query tiles along the Gilbert curve of the 64x64
+    token grid (exact and App. B importances; M0 = 256 for the latter)."""
+    over = dict(M0=256, P=32) if approx else {}
+    data = _data("grid64", **over)
+    order = gilbert.query_order(64, 64)
+    _ordered_check(_place_along(data, order), data["cfg"].P, order, approx=approx)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ordered_random_ragged(dtype):
+    """A random order over a ragged query count (not a whole number of tiles),
+    with the last positions naming no row: those rows stay as they were."""
+    data = _data("grid64", N=2048 + 64 + 5, grid=None, dtype=dtype, H=2)
+    N = data["cfg"].N
+    order = np.random.default_rng(11).permutation(N).astype(np.int32)
+    order[-3:] = [-1, N, -7]
+    _ordered_check(_place_along(data, order), data["cfg"].P, order, nan_fill=True)
+
+
+def test_ordered_identity_is_plain():
+    """The identity order gives avq_attention_fwd's results bit for bit."""
+    data = _data("grid64", N=2048 + 64 + 5, grid=None, H=2)
+    P = data["cfg"].P
+    say("[parity] identity order against the plain call")
+    g0 = run_gpu(data, P)
+    g1 = run_gpu(data, P, order=np.arange(data["cfg"].N, dtype=np.int32))
+    for k in ("Y", "sel", "importance"):
+        assert np.array_equal(g0[k], g1[k]), k
+
+
+def test_ordered_flat_codebook():
+    """P = 0 (plain VQ attention over 256 codewords) along the Gilbert curve."""
+    data = _data("grid64", M0=256, C=0, P=0)
+    order = gilbert.query_order(64, 64)
+    _ordered_check(_place_along(data, order), 0, order)
+
+
 @pytest.mark.parametrize("M0", [64, 256])
 def test_flat_codebook(M0):
     """C = 0: a flat codebook of M0 codewords, plain VQ attention (P = 0)."""
@@ -190,3 +288,34 @@ def test_full_size_grid128():
         assert np.array_equal(g["sel"][bh, t], sel[0, 0]), (bh, t)
         Y = os_.attention_substituted(Qt, cbh, vsum[bh:bh + 1], counts[bh:bh + 1], sel, cfg.P, cfg.block_q, cfg.scale)
         compare_y(g["Y"][bh:bh + 1, i0:i1], Y, cfg.dtype, f"grid128 bh{bh} tile{t}")
+
+
+def test_full_size_grid128_gilbert():
+    """The headline workload at full size with its queries along the Gilbert
+    curve of the 128x128 grid, in the launch configuration the benchmark times
+    with --query-order gilbert: sampled tiles checked one by one."""
+    data = _data("grid128")
+    cfg = data["cfg"]
+    order = gilbert.query_order(128, 128)
+    d2 = _place_along(data, order)
+    say(f"[parity] grid128 full size, Gilbert order B{cfg.B} H{cfg.H} N{cfg.N}")
+    g = run_gpu(d2, cfg.P, order=order)
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(g["row"], row)
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    assert np.array_equal(g["counts"], counts)
+    rng = np.random.default_rng(8)
+    bq = cfg.block_q
+    picks = [(int(rng.integers(cfg.BH)), int(rng.integers(cfg.tiles))) for _ in range(32)] + [(cfg.BH - 1, cfg.tiles - 1)]
+    for bh, t in picks:
+        h = bh % cfg.H
+        rows = order[t * bq:(t + 1) * bq]
+        Qt = d2["Q"][bh:bh + 1, rows]
+        os_ = oracle.Oracle(1, 1, len(rows), cfg.d, cfg.M0, cfg.C)
+        cbh = data["codebook"][h:h + 1]
+        w = os_.importance(Qt, cbh, counts[bh:bh + 1], bq, cfg.scale)
+        sel = os_.select(w, cfg.P)
+        assert np.array_equal(g["sel"][bh, t], sel[0, 0]), (bh, t)
+        Y = os_.attention_substituted(Qt, cbh, vsum[bh:bh + 1], counts[bh:bh + 1], sel, cfg.P, bq, cfg.scale)
+        compare_y(g["Y"][bh:bh + 1, rows], Y, cfg.dtype, f"grid128 Gilbert bh{bh} tile{t}")
