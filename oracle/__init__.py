@@ -52,6 +52,7 @@ def load(path: Optional[str] = None):
     lib.avqo_tile_margin.argtypes = [i32, i32, i32, P, P, P, i32, dbl]
     lib.avqo_tile_margin.restype = dbl
     lib.avqo_tile_margins.argtypes = [i32] * 6 + [P, P, P, i32, i32, dbl, P]
+    lib.avqo_codebook_update_f64.argtypes = [i32] * 5 + [P, P, dbl, P, P, P]
     if path is None:
         _lib = lib
     return lib
@@ -183,6 +184,17 @@ class Oracle:
         out = np.full((self.B * self.H, self.tiles(bq)), np.inf)
         _ok(self.lib.avqo_tile_margins(*self.dims, _p(Q), _p(cb), _p(counts), bq, P, scale, _p(out)))
         return out
+
+    # App. A, Eq. 11-12 (training): EMA statistics and constrained positions
+    def codebook_update(self, ksum, counts, decay: float, S, Nm, codebook):
+        """One update step from the batch's per-codeword key sums and counts
+        (``aggregate`` with the keys as values).  Returns new (S [H, Mt, d],
+        N [H, Mt], codebook [H, Mt, d]) in double; the inputs are not changed."""
+        ksum, counts = _f64(ksum), _i32(counts)
+        S, Nm, cb = _f64(S).copy(), _f64(Nm).copy(), _f64(codebook).copy()
+        _ok(self.lib.avqo_codebook_update_f64(self.B, self.H, self.d, self.M0, self.C, _p(ksum), _p(counts),
+                                              float(decay), _p(S), _p(Nm), _p(cb)))
+        return S, Nm, cb
 
     # Sec. 4.3 and Fig. 3: query tiles taken along a token order
     def ordered(self, Q, order):

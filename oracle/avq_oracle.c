@@ -44,6 +44,13 @@
  *   avqo_exact_attention      equal keys, a two-key closed form, keys = parents
  *   avqo_key_margins,
  *   avqo_tile_margin(s)       hand-computed tie distances
+ *   avqo_codebook_update_f64  the constraint holds exactly; the children solve
+ *                             the weighted least-squares problem (against an
+ *                             independent KKT solve and against feasible
+ *                             perturbations); N_c times the displacement is
+ *                             the same for every child; equal masses shift
+ *                             every child alike; decay 0 gives the cell means
+ *                             of the keys; massless children take the residual
  * No function is left unpinned.
  */
 #include <math.h>
@@ -647,6 +654,84 @@ int avqo_importance_tiled_f64(int B, int H, int N, int d, int M0, int C,
         free(s);
     }
     return ORACLE_OK;
+}
+
+/* App. A, Eq. 11 and Eq. 12: one codebook-update step (training), per head.
+ *
+ * ksum [B*H][Mt][d], counts [B*H][Mt]: the keys of this batch summed per
+ *   codeword and counted, parents over their whole cell and children over the
+ *   keys that moved to them (the aggregation of Eq. 3 with the keys in place
+ *   of the values; Fig. 2 steps 3 and 4).
+ * S [H][Mt][d], Nm [H][Mt]: the EMA statistics (S_x, N_x), updated in place
+ *   by Eq. 11 with the batch's sums over all b of the head (one codebook per
+ *   head, Sec. 4.1): S <- decay S + (1 - decay) sum k, N <- decay N + (1 -
+ *   decay) |{k}|.
+ * cb [H][Mt][d]: the codeword positions, updated in place.  A parent moves to
+ *   its mean M_p = S_p / N_p (it keeps its position while N_p = 0).  Its
+ *   children move to the solution of the mass-weighted least-squares problem
+ *   of App. A (minimise sum_c N_c |M_c - C_pc|^2 subject to the mean of the
+ *   children being the new parent): Eq. 12, C_pc = M_c - delta / (N_c sigma)
+ *   with M_c = S_c / N_c, delta = sum_c M_c - C C_p, sigma = sum_c 1 / N_c.
+ *   A child with N_c = 0 has no mean: its current position stands for M_c,
+ *   and, having no mass, it takes the whole residual -- the limit of Eq. 12
+ *   as its N_c goes to zero: each of the |Z| massless children moves by
+ *   -delta / |Z| and the others keep their means.
+ */
+int avqo_codebook_update_f64(int B, int H, int d, int M0, int C, const double* ksum, const int32_t* counts,
+                             double decay, double* S, double* Nm, double* cb) {
+  if (B < 0 || H < 0 || d < 1 || M0 < 1 || C < 0 || !(decay >= 0.0 && decay <= 1.0)) return ORACLE_ERR;
+  const int64_t Mt = mt_of(M0, C);
+  double* kb = (double*)malloc(sizeof(double) * (size_t)d);
+  double* M = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1) * (size_t)d);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!kb || !M || !delta) { free(kb); free(M); free(delta); return ORACLE_ERR; }
+  for (int h = 0; h < H; ++h) {
+    double* Sh = S + (int64_t)h * Mt * d;
+    double* Nh = Nm + (int64_t)h * Mt;
+    double* cbh = cb + (int64_t)h * Mt * d;
+    /* Eq. 11 for every codeword of the head */
+    for (int64_t x = 0; x < Mt; ++x) {
+      double cnt = 0.0;
+      for (int t = 0; t < d; ++t) kb[t] = 0.0;
+      for (int b = 0; b < B; ++b) {
+        const int64_t bh = (int64_t)b * H + h;
+        cnt += (double)counts[bh * Mt + x];
+        for (int t = 0; t < d; ++t) kb[t] += ksum[(bh * Mt + x) * d + t];
+      }
+      for (int t = 0; t < d; ++t) Sh[x * d + t] = decay * Sh[x * d + t] + (1.0 - decay) * kb[t];
+      Nh[x] = decay * Nh[x] + (1.0 - decay) * cnt;
+    }
+    for (int p = 0; p < M0; ++p) {
+      /* the parent: its unconstrained mean, no constraint */
+      if (Nh[p] > 0.0)
+        for (int t = 0; t < d; ++t) cbh[(int64_t)p * d + t] = Sh[(int64_t)p * d + t] / Nh[p];
+      if (C == 0) continue;
+      /* the children: unconstrained means, then Eq. 12 */
+      const int64_t c0 = M0 + (int64_t)p * C;
+      int zeros = 0;
+      double sigma = 0.0;
+      for (int c = 0; c < C; ++c) {
+        const double n = Nh[c0 + c];
+        for (int t = 0; t < d; ++t)
+          M[c * d + t] = n > 0.0 ? Sh[(c0 + c) * d + t] / n : cbh[(c0 + c) * d + t];
+        if (n > 0.0) sigma += 1.0 / n; else ++zeros;
+      }
+      for (int t = 0; t < d; ++t) {
+        double sm = 0.0;
+        for (int c = 0; c < C; ++c) sm += M[c * d + t];
+        delta[t] = sm - (double)C * cbh[(int64_t)p * d + t];
+      }
+      for (int c = 0; c < C; ++c) {
+        const double n = Nh[c0 + c];
+        double share;                      /* the part of delta this child takes */
+        if (zeros == 0) share = 1.0 / (n * sigma);
+        else share = n > 0.0 ? 0.0 : 1.0 / zeros;
+        for (int t = 0; t < d; ++t) cbh[(c0 + c) * d + t] = M[c * d + t] - share * delta[t];
+      }
+    }
+  }
+  free(kb); free(M); free(delta);
+  return ORACLE_OK;
 }
 
 int avqo_version(void) { return 1; }

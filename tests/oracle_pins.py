@@ -528,6 +528,157 @@ def pin_order_trailing_empty(lib):
     np.testing.assert_allclose(w[:, T - 1].sum(-1), bq - 5, rtol=1e-12)
 
 
+# ---------------------------------------------------------------- codebook update (App. A)
+def _update_case(seed, B=2, H=2, d=5, M0=3, C=4, zero_child=None, zero_parent=None):
+    """Random EMA state, positions and batch statistics of a small codebook."""
+    rng = np.random.default_rng(seed)
+    Mt = M0 * (1 + C)
+    S = rng.standard_normal((H, Mt, d)) * 3.0
+    Nm = rng.uniform(0.5, 20.0, (H, Mt))
+    cb = rng.standard_normal((H, Mt, d))
+    counts = rng.integers(0, 9, (B * H, Mt)).astype(np.int32)
+    ksum = rng.standard_normal((B * H, Mt, d)) * counts[..., None]
+    for h, x in (zero_child or []) + (zero_parent or []):
+        Nm[h, x] = 0.0
+        S[h, x] = 0.0
+        counts[h::H, x] = 0
+        ksum[h::H, x] = 0.0
+    return dict(B=B, H=H, d=d, M0=M0, C=C, S=S, Nm=Nm, cb=cb, counts=counts, ksum=ksum)
+
+
+def _update(lib, c, decay):
+    o = _O(lib, c["B"], c["H"], 1, c["d"], c["M0"], c["C"])
+    return o.codebook_update(c["ksum"], c["counts"], decay, c["S"], c["Nm"], c["cb"])
+
+
+def _kkt_children(Mc, Nc, target):
+    """The constrained weighted least-squares problem of App. A solved as a
+    linear KKT system (numpy), one coordinate at a time: minimise
+    sum_c N_c (M_c - x_c)^2 subject to sum_c x_c = target."""
+    Cn, d = Mc.shape
+    X = np.zeros_like(Mc)
+    for t in range(d):
+        A = np.zeros((Cn + 1, Cn + 1))
+        rhs = np.zeros(Cn + 1)
+        for c in range(Cn):
+            A[c, c] = 2.0 * Nc[c]
+            A[c, Cn] = 1.0
+            A[Cn, c] = 1.0
+            rhs[c] = 2.0 * Nc[c] * Mc[c, t]
+        rhs[Cn] = target[t]
+        X[:, t] = np.linalg.solve(A, rhs)[:Cn]
+    return X
+
+
+def pin_update_projection(lib):
+    """App. A: after the update every parent is the mean of its children
+    (Eq. 5), and the children solve the mass-weighted least-squares problem:
+    they equal an independent KKT solve, every feasible perturbation raises the
+    objective, and N_c times each child's displacement from its mean is the same
+    vector for all children (heavier children move less, Fig. 2 step 5)."""
+    c = _update_case(61)
+    S, Nm, cb = _update(lib, c, 0.9)
+    M0, C = c["M0"], c["C"]
+    rng = np.random.default_rng(1)
+    for h in range(c["H"]):
+        for p in range(M0):
+            kids = slice(M0 + p * C, M0 + (p + 1) * C)
+            np.testing.assert_allclose(cb[h, kids].mean(0), cb[h, p], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(cb[h, p], S[h, p] / Nm[h, p], rtol=1e-13)
+            Mc, Nc = S[h, kids] / Nm[h, kids][:, None], Nm[h, kids]
+            np.testing.assert_allclose(cb[h, kids], _kkt_children(Mc, Nc, C * cb[h, p]), rtol=1e-9, atol=1e-10)
+
+            def obj(X):
+                return float((Nc[:, None] * (Mc - X) ** 2).sum())
+            base = obj(cb[h, kids])
+            for _ in range(5):
+                D = rng.standard_normal(Mc.shape)
+                D -= D.mean(0)          # keeps the mean of the children
+                assert obj(cb[h, kids] + 1e-3 * D) > base
+            disp = Nc[:, None] * (Mc - cb[h, kids])
+            np.testing.assert_allclose(disp, np.broadcast_to(disp[0], disp.shape), rtol=1e-9, atol=1e-10)
+
+
+def pin_update_ema(lib):
+    """Eq. 11 and the parent rule on cases with a plain answer: decay 0 moves
+    every parent to the mean of the keys of its cell over the whole batch
+    (computed here from the keys and the oracle's assignment) and sets N to
+    the cell's key count; decay 1 leaves the statistics as they were; two steps
+    from a zero state give S = decay (1 - decay) k_1 + (1 - decay) k_2."""
+    cfg, data = _small_case(67, N=96, d=6, M0=4, C=3)
+    cfg = cfg.replace(B=2, H=2)
+    data = gen.make(cfg)
+    o = _O(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C)
+    parent, row = o.assign(data["K"], data["codebook"])
+    ksum, counts = o.aggregate(data["K"], parent, row)
+    Mt = cfg.Mt
+    zS, zN = np.zeros((cfg.H, Mt, cfg.d)), np.zeros((cfg.H, Mt))
+    S, Nm, cb = o.codebook_update(ksum, counts, 0.0, zS, zN, data["codebook"])
+    K = data["K"].astype(np.float64)
+    for h in range(cfg.H):
+        for p in range(cfg.M0):
+            keys = np.concatenate([K[b * cfg.H + h][parent[b * cfg.H + h] == p] for b in range(cfg.B)])
+            assert Nm[h, p] == len(keys)
+            if len(keys):
+                np.testing.assert_allclose(cb[h, p], keys.mean(0), rtol=1e-12, atol=1e-12)
+            else:
+                assert np.array_equal(cb[h, p], data["codebook"][h, p])
+    S1, N1, _ = o.codebook_update(ksum, counts, 1.0, S, Nm, cb)
+    assert np.array_equal(S1, S) and np.array_equal(N1, Nm)
+    lam = 0.8
+    ks2 = ksum[::-1].copy()
+    c2 = counts[::-1].copy()
+    Sa, Na, _ = o.codebook_update(ksum, counts, lam, zS, zN, data["codebook"])
+    Sb, Nb, _ = o.codebook_update(ks2, c2, lam, Sa, Na, data["codebook"])
+    k1 = ksum.reshape(cfg.B, cfg.H, Mt, cfg.d).sum(0)
+    k2 = ks2.reshape(cfg.B, cfg.H, Mt, cfg.d).sum(0)
+    n1 = counts.reshape(cfg.B, cfg.H, Mt).sum(0)
+    n2 = c2.reshape(cfg.B, cfg.H, Mt).sum(0)
+    np.testing.assert_allclose(Sb, lam * (1 - lam) * k1 + (1 - lam) * k2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Nb, lam * (1 - lam) * n1 + (1 - lam) * n2, rtol=1e-12)
+
+
+def pin_update_special_cases(lib):
+    """Eq. 12's special cases: equal masses shift every child by the same
+    delta / C; children whose means already average to the parent stay at
+    their means; a massless child takes the whole residual and the others keep
+    their means; a parent that has never had a key keeps its position and its
+    children are projected onto it; a flat codebook (C = 0) moves every
+    codeword to its mean."""
+    c = _update_case(71, B=1, H=1, M0=2, C=3)
+    c["Nm"][:] = 4.0
+    c["counts"][:] = 2
+    S, Nm, cb = _update(lib, c, 0.5)
+    for p in range(2):
+        kids = slice(2 + 3 * p, 2 + 3 * (p + 1))
+        Mc = S[0, kids] / Nm[0, kids][:, None]
+        delta = Mc.sum(0) - 3 * cb[0, p]
+        np.testing.assert_allclose(cb[0, kids], Mc - delta / 3, rtol=1e-12, atol=1e-12)
+    # means that already average to the parent: decay 1 over a state built that way
+    c = _update_case(73, B=1, H=1, M0=1, C=3)
+    Mc = np.random.default_rng(2).standard_normal((3, c["d"]))
+    c["Nm"][0] = [2.0, 1.0, 3.0, 5.0]
+    c["S"][0, 0] = Mc.mean(0) * 2.0
+    c["S"][0, 1:] = Mc * np.array([1.0, 3.0, 5.0])[:, None]
+    _, _, cb = _update(lib, c, 1.0)
+    np.testing.assert_allclose(cb[0, 1:], Mc, rtol=1e-12, atol=1e-12)
+    # a massless child (h 0, child 1 of parent 0), a never-seen parent (h 1, parent 2)
+    c = _update_case(79, zero_child=[(0, 3 + 1)], zero_parent=[(1, 2)])
+    S, Nm, cb = _update(lib, c, 0.7)
+    kids = slice(3, 7)
+    Mc = S[0, kids] / np.where(Nm[0, kids] > 0, Nm[0, kids], 1.0)[:, None]
+    Mc[1] = c["cb"][0, 4]
+    delta = Mc.sum(0) - 4 * cb[0, 0]
+    np.testing.assert_allclose(cb[0, kids][[0, 2, 3]], Mc[[0, 2, 3]], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(cb[0, 4], Mc[1] - delta, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(cb[1, 2], c["cb"][1, 2])
+    np.testing.assert_allclose(cb[1, 3 + 8:3 + 12].mean(0), c["cb"][1, 2], rtol=1e-12, atol=1e-12)
+    # flat codebook
+    c = _update_case(83, C=0)
+    S, Nm, cb = _update(lib, c, 0.3)
+    np.testing.assert_allclose(cb, S / Nm[..., None], rtol=1e-13)
+
+
 PINS = {
     "assign_ground_truth": pin_assign_ground_truth,
     "assign_copies": pin_assign_copies,
@@ -549,4 +700,7 @@ PINS = {
     "order_tile_relabel": pin_order_tile_relabel,
     "order_homogeneous_tiles": pin_order_homogeneous_tiles,
     "order_trailing_empty": pin_order_trailing_empty,
+    "update_projection": pin_update_projection,
+    "update_ema": pin_update_ema,
+    "update_special_cases": pin_update_special_cases,
 }

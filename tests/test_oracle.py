@@ -47,6 +47,15 @@ MUTANTS = [
      "zacc = m == -INFINITY ? 0.0 : zacc;"),
     ("keys of a tile's first parent not seen", "                        nseen += n[j];",
      "                        nseen += (j > j0) ? n[j] : 0;"),
+    ("harmonic weight sums the masses", "if (n > 0.0) sigma += 1.0 / n; else ++zeros;",
+     "if (n > 0.0) sigma += n; else ++zeros;"),
+    ("residual without the child count", "delta[t] = sm - (double)C * cbh[(int64_t)p * d + t];",
+     "delta[t] = sm - cbh[(int64_t)p * d + t];"),
+    ("EMA weights swapped", "Sh[x * d + t] = decay * Sh[x * d + t] + (1.0 - decay) * kb[t];",
+     "Sh[x * d + t] = (1.0 - decay) * Sh[x * d + t] + decay * kb[t];"),
+    ("unweighted projection", "if (zeros == 0) share = 1.0 / (n * sigma);", "if (zeros == 0) share = 1.0 / C;"),
+    ("massless children keep their place", "else share = n > 0.0 ? 0.0 : 1.0 / zeros;", "else share = 0.0;"),
+    ("count EMA uses the old count twice", "Nh[x] = decay * Nh[x] + (1.0 - decay) * cnt;", "Nh[x] = decay * Nh[x] + (1.0 - decay) * Nh[x];"),
 ]
 
 
