@@ -44,6 +44,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avq_attention_fwd_ordered.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, i32, P, P, P, P,
                                                                       ctypes.c_size_t, P]
     lib.avq_attention_fwd_ordered.restype = i32
+    lib.avq_codebook_update.argtypes = [P, P] + [i32] * 5 + [f32, P, P, P, P]
+    lib.avq_codebook_update.restype = i32
     lib.avq_attention_workspace_size.argtypes = [i32] * 6
     lib.avq_attention_workspace_size.restype = ctypes.c_size_t
     lib.avq_status_string.argtypes = [i32]
@@ -176,3 +178,36 @@ def forward(Q, K, V, codebook, C: int, P: int, block_q: int, scale: Optional[flo
     vsum, counts, _ = assign_aggregate(K, V, codebook, C)
     Y, _, _ = attention_fwd(Q, codebook, vsum, counts, C, P, block_q, scale)
     return Y
+
+
+def codebook_update(ksum: torch.Tensor, counts: torch.Tensor, S: torch.Tensor, Nema: torch.Tensor,
+                    codebook: torch.Tensor, C: int, decay: float):
+    """Codebook update step (App. A, Eq. 11-12), in place on S [H, Mt, d], Nema [H, Mt] and
+    codebook [H, Mt, d] (all float32).  ksum [B, H, Mt, d] float32 and counts [B, H, Mt] int32 are
+    this batch's per-codeword key sums and counts: assign_aggregate(K, K, ...)."""
+    if ksum.dim() != 4 or ksum.dtype != torch.float32 or not ksum.is_contiguous():
+        raise ValueError("ksum must be a contiguous float32 [B, H, Mt, d] tensor")
+    B, H, Mt, d = ksum.shape
+    if Mt % (1 + C):
+        raise ValueError("codeword rows must be M0 * (1 + C)")
+    M0 = Mt // (1 + C)
+    if tuple(counts.shape) != (B, H, Mt) or counts.dtype != torch.int32 or not counts.is_contiguous():
+        raise ValueError("counts must be a contiguous int32 [B, H, Mt] tensor")
+    for name, t, shape in (("S", S, (H, Mt, d)), ("Nema", Nema, (H, Mt)), ("codebook", codebook, (H, Mt, d))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor")
+    rc = _lib.avq_codebook_update(_ptr(ksum), _ptr(counts), B, H, d, M0, C, float(decay), _ptr(S), _ptr(Nema),
+                                  _ptr(codebook), _stream(S))
+    if rc != 0:
+        raise AvqError(rc, "avq_codebook_update")
+    return S, Nema, codebook
+
+
+def update_codebook(K: torch.Tensor, codebook: torch.Tensor, S: torch.Tensor, Nema: torch.Tensor, C: int,
+                    decay: float):
+    """One training step of the codebook from the keys K [B, H, N, d]: the keys are assigned and
+    summed per codeword against the codebook rounded to K's dtype (assign_aggregate with V = K),
+    then codebook_update moves the float32 positions in place.  Returns (S, Nema, codebook)."""
+    cb_in = codebook if K.dtype == torch.float32 else codebook.to(K.dtype).contiguous()
+    ksum, counts, _ = assign_aggregate(K, K, cb_in, C)
+    return codebook_update(ksum, counts, S, Nema, codebook, C, decay)

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libavq.so")
-SOURCES = ["api.hip", "assign_aggregate.hip", "attention.hip"]
+SOURCES = ["api.hip", "assign_aggregate.hip", "attention.hip", "codebook_update.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -126,6 +126,19 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                         workspace, workspace_bytes, stream, approx_denominator != 0, query_order, true);
 }
 
+int avq_codebook_update(const float* ksum, const int32_t* counts, int B, int H, int d, int M0, int C, float decay,
+                        float* S, float* Nema, float* codebook, void* stream) {
+  if (B < 0 || H < 0 || d < 1 || M0 < 1 || C < 0) return AVQ_ERR_SHAPE;
+  if (!(decay >= 0.0f && decay <= 1.0f)) return AVQ_ERR_SHAPE;  // NaN included
+  if (C > 16 || (int64_t)H * M0 > (int64_t)1 << 30) return AVQ_ERR_UNSUPPORTED;
+  if (H == 0) return AVQ_OK;
+  if (!S || !Nema || !codebook || (B > 0 && (!ksum || !counts))) return AVQ_ERR_NULL;
+  auto a4 = [](const void* q) { return ((uintptr_t)q & 3u) == 0; };
+  if (!a4(S) || !a4(Nema) || !a4(codebook) || !a4(ksum) || !a4(counts)) return AVQ_ERR_ALIGN;
+  return from_hip(avq::launch_codebook_update(ksum, counts, B, H, d, M0, C, decay, S, Nema, codebook,
+                                              (hipStream_t)stream));
+}
+
 const char* avq_status_string(int status) {
   switch (status) {
     case AVQ_OK: return "ok";
@@ -133,7 +146,7 @@ const char* avq_status_string(int status) {
     case AVQ_ERR_SHAPE: return "a size is out of range";
     case AVQ_ERR_DTYPE: return "unknown dtype";
     case AVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case AVQ_ERR_UNSUPPORTED: return "unsupported size (d, M0, C, block_q or B*H)";
+    case AVQ_ERR_UNSUPPORTED: return "unsupported size (d, M0, C, block_q, B*H or H*M0)";
     case AVQ_ERR_HIP: return "HIP runtime error";
     case AVQ_ERR_WORKSPACE: return "workspace smaller than avq_attention_workspace_size()";
     default: return "unknown status";

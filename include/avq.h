@@ -204,6 +204,45 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                               float* Y, int32_t* topp, float* importance,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Codebook update step of the training recipe (App. A, Eq. 11 and Eq. 12;
+ * Sec. 4.1, Fig. 2): one step of EMA online k-means on the hierarchical
+ * codebook of every head, with the parent-child constraint restored.
+ *
+ *   ksum     in  [B*H, Mt, d] float: this batch's keys summed per codeword,
+ *                parents over their whole cell and children over the keys
+ *                that moved to them -- the vsum of avq_assign_aggregate
+ *                called with the keys as the values (V = K)
+ *   counts   in  [B*H, Mt] int32: the matching key counts (its counts)
+ *   decay    the EMA decay lambda, 0 <= decay <= 1
+ *   S        in/out [H, Mt, d] float: EMA key sums S_x (Eq. 11)
+ *   Nema     in/out [H, Mt] float: EMA key counts N_x (Eq. 11)
+ *   codebook in/out [H, Mt, d] float: the codeword positions
+ *
+ * For every head h and codeword x, with the batch totals over b = 0..B-1:
+ *   S_x <- decay S_x + (1 - decay) sum_b ksum[b*H+h, x]
+ *   N_x <- decay N_x + (1 - decay) sum_b counts[b*H+h, x]
+ * a parent moves to its mean S_p / N_p (it keeps its position while
+ * N_p = 0), and its children to the minimiser of sum_c N_c |M_c - C_pc|^2
+ * with mean_c C_pc = C_p, M_c = S_c / N_c (Eq. 12):
+ *   C_pc = M_c - delta / (N_c sigma), delta = sum_c M_c - C C_p,
+ *   sigma = sum_c 1 / N_c.
+ * A child with N_c = 0 has no mean: its current position stands for M_c, and
+ * the children without mass share the whole residual equally (the limit of
+ * Eq. 12 as their mass goes to zero), the others keeping their means.  With
+ * C = 0 every codeword moves to its mean.  Arithmetic is float; the
+ * constraint then holds to float rounding (a bf16 copy of the codebook for
+ * the forward calls holds it to bf16 rounding).
+ *
+ * Sizes: d >= 1, C <= 16, H*M0 <= 2^30 (AVQ_ERR_UNSUPPORTED otherwise); B may
+ * be 0 (pure decay; ksum and counts may then be NULL).  All pointers 4-byte
+ * aligned (AVQ_ERR_ALIGN).  S, Nema and codebook are updated in place; the
+ * three must not overlap each other or the inputs.  Allocates nothing.
+ */
+int avq_codebook_update(const float* ksum, const int32_t* counts, int B, int H, int d, int M0,
+                        int C, float decay, float* S, float* Nema, float* codebook,
+                        void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* avq_status_string(int status);
 

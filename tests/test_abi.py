@@ -22,8 +22,8 @@ def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
     assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_attention_fwd_approx",
-                          "avq_attention_fwd_ordered", "avq_attention_workspace_size", "avq_status_string",
-                          "avq_version"}
+                          "avq_attention_fwd_ordered", "avq_attention_workspace_size", "avq_codebook_update",
+                          "avq_status_string", "avq_version"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -135,3 +135,27 @@ def test_binding_fails_loudly_without_library(tmp_path):
     from adaptive_vector_quantized_amd import _lib
     with pytest.raises(ImportError):
         _lib._load(str(tmp_path / "missing.so"))
+
+
+def test_codebook_update_validation(L):
+    _, p = _buf()
+
+    def upd(**kw):
+        a = dict(ksum=p, counts=p, B=2, H=1, d=64, M0=4, C=2, decay=0.99, S=p, N=p, cb=p)
+        a.update(kw)
+        return L.avq_codebook_update(a["ksum"], a["counts"], a["B"], a["H"], a["d"], a["M0"], a["C"], a["decay"],
+                                     a["S"], a["N"], a["cb"], None)
+    assert upd(decay=-0.1) == -2
+    assert upd(decay=1.5) == -2
+    assert upd(decay=float("nan")) == -2
+    assert upd(d=0) == -2
+    assert upd(M0=0) == -2
+    assert upd(C=-1) == -2
+    assert upd(B=-1) == -2
+    assert upd(C=17) == -5
+    assert upd(S=None) == -1
+    assert upd(N=None) == -1
+    assert upd(cb=None) == -1
+    assert upd(ksum=None) == -1
+    assert upd(counts=ctypes.c_void_p(p.value + 2)) == -4
+    assert upd(H=0, S=None) == 0      # no head: nothing to do
