@@ -38,6 +38,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.avq_assign_aggregate.argtypes = [P, P, P] + [i32] * 7 + [P, P, P, P]
     lib.avq_assign_aggregate.restype = i32
+    lib.avq_assign_aggregate_kv.argtypes = [P, P, P] + [i32] * 7 + [P, P, P, P, P]
+    lib.avq_assign_aggregate_kv.restype = i32
     for f in (lib.avq_attention_fwd, lib.avq_attention_fwd_approx):
         f.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P, ctypes.c_size_t, P]
         f.restype = i32
@@ -117,6 +119,37 @@ def assign_aggregate(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C
     if rc != 0:
         raise AvqError(rc, "avq_assign_aggregate")
     return vsum, counts, assign
+
+
+def assign_aggregate_kv(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C: int, *,
+                        want_assign: bool = False, vsum: Optional[torch.Tensor] = None,
+                        counts: Optional[torch.Tensor] = None, assign: Optional[torch.Tensor] = None,
+                        ksum: Optional[torch.Tensor] = None):
+    """Kernel 1 with the keys also summed per codeword (for codebook_update), in one pass.
+    Returns (vsum, counts, assign or None, ksum [B, H, Mt, d] float32)."""
+    B, H, N, d = _shape4(K, "K")
+    if tuple(V.shape) != (B, H, N, d) or V.dtype != K.dtype or not V.is_contiguous():
+        raise ValueError("V must match K")
+    if codebook.dim() != 3 or codebook.shape[0] != H or codebook.shape[2] != d or not codebook.is_contiguous():
+        raise ValueError("codebook must be a contiguous [H, Mt, d] tensor")
+    Mt = codebook.shape[1]
+    if Mt % (1 + C):
+        raise ValueError("codebook rows must be M0 * (1 + C)")
+    M0 = Mt // (1 + C)
+    dev = K.device
+    if vsum is None:
+        vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
+    if ksum is None:
+        ksum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
+    if want_assign and assign is None:
+        assign = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    rc = _lib.avq_assign_aggregate_kv(_ptr(K), _ptr(V), _ptr(codebook), B, H, N, d, M0, C, _dtype_code(K),
+                                      _ptr(vsum), _ptr(counts), _ptr(assign), _ptr(ksum), _stream(K))
+    if rc != 0:
+        raise AvqError(rc, "avq_assign_aggregate_kv")
+    return vsum, counts, assign, ksum
 
 
 def workspace_size(B: int, H: int, d: int, M0: int, C: int, dtype: torch.dtype) -> int:

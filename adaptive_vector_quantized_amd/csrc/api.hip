@@ -45,26 +45,42 @@ hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
 
 }  // namespace avq
 
-extern "C" {
+namespace {
 
-int avq_assign_aggregate(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0, int C,
-                         int dtype, float* vsum, int32_t* counts, int32_t* assign, void* stream) {
+int assign_call(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0, int C,
+                int dtype, float* vsum, int32_t* counts, int32_t* assign, float* ksum, bool with_keys, void* stream) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
   const int64_t BH = (int64_t)B * H;
   if (BH == 0) return AVQ_OK;
-  if (!vsum || !counts || !codebook) return AVQ_ERR_NULL;
+  if (!vsum || !counts || !codebook || (with_keys && !ksum)) return AVQ_ERR_NULL;
   if (N > 0 && (!K || !V)) return AVQ_ERR_NULL;
   if (!aligned16(vsum) || !aligned16(counts) || !aligned16(codebook) || (K && !aligned16(K)) ||
-      (V && !aligned16(V)) || (assign && !aligned16(assign)))
+      (V && !aligned16(V)) || (assign && !aligned16(assign)) || (ksum && !aligned16(ksum)))
     return AVQ_ERR_ALIGN;
   if (avq::assign_smem_bytes(dtype, d, M0, C) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
   const int64_t Mt = (int64_t)M0 * (1 + C);
   hipStream_t st = (hipStream_t)stream;
   rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, counts, BH * Mt, st));
+  if (rc == AVQ_OK && with_keys) rc = from_hip(avq::launch_zero(ksum, BH * Mt * d, nullptr, 0, st));
   if (rc != AVQ_OK || N == 0) return rc;
-  return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, vsum, counts,
-                                     assign, st));
+  return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, vsum, counts, assign,
+                                     with_keys ? ksum : nullptr, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int avq_assign_aggregate(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0, int C,
+                         int dtype, float* vsum, int32_t* counts, int32_t* assign, void* stream) {
+  return assign_call(K, V, codebook, B, H, N, d, M0, C, dtype, vsum, counts, assign, nullptr, false, stream);
+}
+
+int avq_assign_aggregate_kv(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0,
+                            int C, int dtype, float* vsum, int32_t* counts, int32_t* assign, float* ksum,
+                            void* stream) {
+  return assign_call(K, V, codebook, B, H, N, d, M0, C, dtype, vsum, counts, assign, ksum, true, stream);
 }
 
 size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C, int dtype) {

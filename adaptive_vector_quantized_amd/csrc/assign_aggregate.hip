@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PL ? Assign
                                                                           : AssignShape<T, D>::kWavesL2))) void
 assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T::in_t* __restrict__ V,
                         const typename T::in_t* __restrict__ cb, int H, int N, int M0, int C,
-                        AssignLds L, float* __restrict__ vsum, int* __restrict__ counts, int* __restrict__ assign) {
+                        AssignLds L, float* __restrict__ vsum, int* __restrict__ counts, int* __restrict__ assign,
+                        float* __restrict__ ksum) {
   using in_t = typename T::in_t;
   using frag_t = typename T::frag_t;
   using Sh = AssignShape<T, D>;
@@ -346,15 +347,16 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // past the end of the sequence read as zero (descriptor bound).
   constexpr int KH = KPW / 2;
   raw_t vr[KH];
-  {
+  auto load_rows = [&](const in_t* src) {
     const int w0 = __builtin_amdgcn_readfirstlane(wave * KPW);
     const int nk = __builtin_amdgcn_readfirstlane(max(0, min(KPW, nval - w0)));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(Vb + (int64_t)(cstart + w0) * D), 0, nk * D * (int)sizeof(in_t), kBufWord3);
+        (void*)(src + (int64_t)(cstart + w0) * D), 0, nk * D * (int)sizeof(in_t), kBufWord3);
     const int voff = (hh * KH * D + ql * EPL) * (int)sizeof(in_t);
 #pragma unroll
     for (int u = 0; u < KH; ++u) vr[u] = buf_load<raw_t>(rs, voff, u * D * (int)sizeof(in_t));
-  }
+  };
+  load_rows(Vb);
   lds_barrier();
 
   // ---- slots: thread p owns parent p (M0 <= 256) and its C children -------
@@ -408,7 +410,9 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // key contributes to the slot of its parent and, if it moved, of its child.
   // Each wave reduces its own keys; the four partial tiles meet in LDS and
   // one atomic row update per touched codeword goes to HBM.
-  float* vsb = vsum + (int64_t)bh * Mt * D;
+  // With ksum the same sums are then formed for the keys (reloaded into the
+  // same registers; the chunk's keys were read moments before, mostly from L2):
+  // the per-codeword key sums of the codebook update (App. A, Eq. 11).
   float* tile = sAcc;  // [4 waves][32 slots][D]
   // one-hot A operand of the wave in LDS, over the bytes of its partial tile:
   // [half][k-step][slot row][E keys] (bf16 1.0 or 0; fp32 for E = 1)
@@ -417,88 +421,97 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   constexpr int NPASS = D / ACC_D;
   oh_t* oh = (oh_t*)(tile + wave * 32 * ACC_D);
   constexpr int OHN = 2 * KH * 32;  // entries
-  for (int sb = 0; sb * 32 < nslots; ++sb) {
-    // clear, then every key marks the rows of its parent and child slots
-    for (int i = lane; i < OHN * (int)sizeof(oh_t) / 16; i += 64) ((u32x4*)oh)[i] = u32x4{0u, 0u, 0u, 0u};
-    __builtin_amdgcn_wave_barrier();
-    for (int kk = lane; kk < KPW; kk += 64) {
-      const int kl = wave * KPW + kk;
-      if (kl < nval) {
-        const uint32_t x = sKS[kl];
-        const int h2 = kk / KH, u = kk % KH;
-        const int base = ((h2 * (KH / E) + u / E) * 32) * E + u % E;
-        const oh_t one = E == 8 ? (oh_t)0x3F80 : (oh_t)1.0f;
-        const int ps = (int)(x & 0xFFFFu) - 32 * sb, cs = (int)(x >> 16) - 32 * sb;
-        if (ps >= 0 && ps < 32) oh[base + ps * E] = one;
-        if (cs >= 0 && cs < 32) oh[base + cs * E] = one;  // 0xFFFF (stayed) is never in range
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    f32x16 acc[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) acc[i] = zero16();
-#pragma unroll
-    for (int t = 0; t < KH / E; ++t) {
-      const oh_t* ap = oh + ((hh * (KH / E) + t) * 32 + ql) * E;
-      frag_t a;
-      if constexpr (E == 8)
-        a = __builtin_bit_cast(frag_t, *(const u32x4*)ap);
-      else
-        a = *ap;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        frag_t b;
-        if constexpr (E == 8) {
-          // element i of E consecutive keys, two bf16 per dword
-          u32x4 w;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t lo, hi;
-            if constexpr (EPL == 2) {
-              lo = vr[8 * t + 2 * q];
-              hi = vr[8 * t + 2 * q + 1];
-            } else {
-              lo = vr[8 * t + 2 * q][i >> 1];
-              hi = vr[8 * t + 2 * q + 1][i >> 1];
-            }
-            w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-          }
-          b = __builtin_bit_cast(frag_t, w);
-        } else {
-          b = vr[t][i];
-        }
-        acc[i] = T::mma_in(a, b, acc[i]);
-      }
-    }
-    // partial tile of this wave (over its one-hot operand): row = slot within
-    // the block, col = dim; ACC_D dims per pass (lane ql holds dims EPL*ql ..)
-    const int nrow = min(32, nslots - 32 * sb);
-#pragma unroll
-    for (int pass = 0; pass < NPASS; ++pass) {
-      if (pass > 0) lds_barrier();  // the previous pass's tiles are summed
+  auto aggregate = [&](float* dst) {
+    float* vsb = dst + (int64_t)bh * Mt * D;
+    for (int sb = 0; sb * 32 < nslots; ++sb) {
+      // clear, then every key marks the rows of its parent and child slots
+      for (int i = lane; i < OHN * (int)sizeof(oh_t) / 16; i += 64) ((u32x4*)oh)[i] = u32x4{0u, 0u, 0u, 0u};
       __builtin_amdgcn_wave_barrier();
-      if (NPASS == 1 || (EPL * ql) / ACC_D == pass) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float* tr = tile + (wave * 32 + row_of(r, hh)) * ACC_D + (EPL * ql) % ACC_D;
-          if constexpr (EPL == 2) {
-            *(f32x2*)tr = f32x2{acc[0][r], acc[1][r]};
-          } else {
-            *(f32x4*)tr = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-          }
+      for (int kk = lane; kk < KPW; kk += 64) {
+        const int kl = wave * KPW + kk;
+        if (kl < nval) {
+          const uint32_t x = sKS[kl];
+          const int h2 = kk / KH, u = kk % KH;
+          const int base = ((h2 * (KH / E) + u / E) * 32) * E + u % E;
+          const oh_t one = E == 8 ? (oh_t)0x3F80 : (oh_t)1.0f;
+          const int ps = (int)(x & 0xFFFFu) - 32 * sb, cs = (int)(x >> 16) - 32 * sb;
+          if (ps >= 0 && ps < 32) oh[base + ps * E] = one;
+          if (cs >= 0 && cs < 32) oh[base + cs * E] = one;  // 0xFFFF (stayed) is never in range
         }
       }
-      lds_barrier();
-      // one row per wave instruction: consecutive lanes, consecutive floats
-      for (int i = tid; i < nrow * ACC_D; i += 256) {
-        const int row = i / ACC_D, c = i % ACC_D;
-        float sum = tile[row * ACC_D + c];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) sum += tile[(w * 32 + row) * ACC_D + c];
-        atomic_add_f32(vsb + (int64_t)sRow[32 * sb + row] * D + pass * ACC_D + c, sum);
+      __builtin_amdgcn_wave_barrier();
+      f32x16 acc[EPL];
+  #pragma unroll
+      for (int i = 0; i < EPL; ++i) acc[i] = zero16();
+  #pragma unroll
+      for (int t = 0; t < KH / E; ++t) {
+        const oh_t* ap = oh + ((hh * (KH / E) + t) * 32 + ql) * E;
+        frag_t a;
+        if constexpr (E == 8)
+          a = __builtin_bit_cast(frag_t, *(const u32x4*)ap);
+        else
+          a = *ap;
+  #pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          frag_t b;
+          if constexpr (E == 8) {
+            // element i of E consecutive keys, two bf16 per dword
+            u32x4 w;
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t lo, hi;
+              if constexpr (EPL == 2) {
+                lo = vr[8 * t + 2 * q];
+                hi = vr[8 * t + 2 * q + 1];
+              } else {
+                lo = vr[8 * t + 2 * q][i >> 1];
+                hi = vr[8 * t + 2 * q + 1][i >> 1];
+              }
+              w[q] = (i & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+            }
+            b = __builtin_bit_cast(frag_t, w);
+          } else {
+            b = vr[t][i];
+          }
+          acc[i] = T::mma_in(a, b, acc[i]);
+        }
       }
+      // partial tile of this wave (over its one-hot operand): row = slot within
+      // the block, col = dim; ACC_D dims per pass (lane ql holds dims EPL*ql ..)
+      const int nrow = min(32, nslots - 32 * sb);
+  #pragma unroll
+      for (int pass = 0; pass < NPASS; ++pass) {
+        if (pass > 0) lds_barrier();  // the previous pass's tiles are summed
+        __builtin_amdgcn_wave_barrier();
+        if (NPASS == 1 || (EPL * ql) / ACC_D == pass) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float* tr = tile + (wave * 32 + row_of(r, hh)) * ACC_D + (EPL * ql) % ACC_D;
+            if constexpr (EPL == 2) {
+              *(f32x2*)tr = f32x2{acc[0][r], acc[1][r]};
+            } else {
+              *(f32x4*)tr = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+            }
+          }
+        }
+        lds_barrier();
+        // one row per wave instruction: consecutive lanes, consecutive floats
+        for (int i = tid; i < nrow * ACC_D; i += 256) {
+          const int row = i / ACC_D, c = i % ACC_D;
+          float sum = tile[row * ACC_D + c];
+  #pragma unroll
+          for (int w = 1; w < 4; ++w) sum += tile[(w * 32 + row) * ACC_D + c];
+          atomic_add_f32(vsb + (int64_t)sRow[32 * sb + row] * D + pass * ACC_D + c, sum);
+        }
+      }
+      if ((sb + 1) * 32 < nslots) lds_barrier();  // the next block rewrites the tiles
     }
-    if ((sb + 1) * 32 < nslots) lds_barrier();  // the next block rewrites the tiles
+  };
+  aggregate(vsum);
+  if (ksum != nullptr) {
+    lds_barrier();  // the last block's tiles are summed before they hold one-hot operands again
+    load_rows(Kb);
+    aggregate(ksum);
   }
 
   // ---- counts --------------------------------------------------------------
@@ -550,7 +563,7 @@ size_t assign_smem_bytes(int dtype, int d, int M0, int C) {
 
 template <class T, int D, int W, bool PL>
 static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, int BH, int H, int N, int M0, int C,
-                                  float* vsum, int* counts, int* assign, hipStream_t st) {
+                                  float* vsum, int* counts, int* assign, float* ksum, hipStream_t st) {
   using Sh = AssignShape<T, D>;
   const AssignLds L = lds_of<T, D>(M0, C, PL);
   auto kern = assign_aggregate_kernel<T, D, W, PL>;
@@ -558,21 +571,21 @@ static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, 
   if (e != hipSuccess) return e;
   dim3 grid((N + Sh::kChunk - 1) / Sh::kChunk, BH);
   hipLaunchKernelGGL(kern, grid, dim3(256), L.total, st, (const typename T::in_t*)K, (const typename T::in_t*)V,
-                     (const typename T::in_t*)cb, H, N, M0, C, L, vsum, counts, assign);
+                     (const typename T::in_t*)cb, H, N, M0, C, L, vsum, counts, assign, ksum);
   return hipGetLastError();
 }
 
 template <class T, int D>
 static hipError_t launch_assign_w(const void* K, const void* V, const void* cb, int BH, int H, int N, int M0, int C,
-                                  float* vsum, int* counts, int* assign, hipStream_t st) {
+                                  float* vsum, int* counts, int* assign, float* ksum, hipStream_t st) {
   if (parents_in_lds<T, D>(M0, C)) {
-    if (C <= 4) return launch_assign_t<T, D, 4, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-    if (C <= 8) return launch_assign_t<T, D, 8, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-    return launch_assign_t<T, D, 16, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+    if (C <= 4) return launch_assign_t<T, D, 4, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
+    if (C <= 8) return launch_assign_t<T, D, 8, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
+    return launch_assign_t<T, D, 16, true>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
   }
-  if (C <= 4) return launch_assign_t<T, D, 4, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-  if (C <= 8) return launch_assign_t<T, D, 8, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-  return launch_assign_t<T, D, 16, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  if (C <= 4) return launch_assign_t<T, D, 4, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
+  if (C <= 8) return launch_assign_t<T, D, 8, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
+  return launch_assign_t<T, D, 16, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
 }
 
 hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st) {
@@ -585,13 +598,13 @@ hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStre
 }
 
 hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
-                         int C, float* vsum, int* counts, int* assign, hipStream_t st) {
+                         int C, float* vsum, int* counts, int* assign, float* ksum, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_assign_w<TF32, 64>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-    return launch_assign_w<TF32, 128>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+    if (d == 64) return launch_assign_w<TF32, 64>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
+    return launch_assign_w<TF32, 128>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
   }
-  if (d == 64) return launch_assign_w<TBF16, 64>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
-  return launch_assign_w<TBF16, 128>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, st);
+  if (d == 64) return launch_assign_w<TBF16, 64>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
+  return launch_assign_w<TBF16, 128>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
 }
 
 }  // namespace avq

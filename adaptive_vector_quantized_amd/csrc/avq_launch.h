@@ -27,7 +27,7 @@ struct AttnTraits {
 
 hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
-                         int C, float* vsum, int* counts, int* assign, hipStream_t st);
+                         int C, float* vsum, int* counts, int* assign, float* ksum, hipStream_t st);
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH);
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,

@@ -127,6 +127,10 @@ def main():
     ap.add_argument("--query-order", choices=("raster", "gilbert"), default="raster",
                     help="query tiles in row-major order, or along the Gilbert curve of the token grid "
                          "(avq_attention_fwd_ordered)")
+    ap.add_argument("--codebook-update", choices=("none", "fused", "separate"), default="none",
+                    help="time the forward pass plus the codebook update of the training recipe (App. A): key sums "
+                         "from avq_assign_aggregate_kv (fused) or from a second aggregation call with V = K "
+                         "(separate), then avq_codebook_update")
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole pass at every refinement budget of the workload (e.g. --workload sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -206,6 +210,60 @@ def main():
         k2 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
         span = ev[0][0].elapsed_time(ev[-1][2]) * 1e-3
         return wall, k1, k2, span
+
+    if args.codebook_update != "none":
+        # forward pass + codebook update: one line with the step rate and per-call times
+        fused = args.codebook_update == "fused"
+        for s_ in sets:
+            s_["ksum"] = torch.empty_like(s_["vsum"])
+            s_["S"] = torch.zeros((cfg.H, cfg.Mt, cfg.d), dtype=torch.float32, device=dev)
+            s_["Nema"] = torch.zeros((cfg.H, cfg.Mt), dtype=torch.float32, device=dev)
+            s_["cb32"] = s_["cb"].float().contiguous()
+
+        def train_step(s_, e=None):
+            if e is not None:
+                e[0].record(stream)
+            if fused:
+                _lib.assign_aggregate_kv(s_["K"], s_["V"], s_["cb"], cfg.C, vsum=s_["vsum"], counts=s_["counts"],
+                                         ksum=s_["ksum"])
+            else:
+                _lib.assign_aggregate(s_["K"], s_["V"], s_["cb"], cfg.C, vsum=s_["vsum"], counts=s_["counts"])
+            if e is not None:
+                e[1].record(stream)
+            _lib.attention_fwd(s_["Q"], s_["cb"], s_["vsum"], s_["counts"], cfg.C, P, cfg.block_q, cfg.scale,
+                               Y=s_["Y"], workspace=s_["ws"])
+            if e is not None:
+                e[2].record(stream)
+            if not fused:
+                _lib.assign_aggregate(s_["K"], s_["K"], s_["cb"], cfg.C, vsum=s_["ksum"], counts=s_["counts"])
+            if e is not None:
+                e[3].record(stream)
+            _lib.codebook_update(s_["ksum"], s_["counts"], s_["S"], s_["Nema"], s_["cb32"], cfg.C, 0.99)
+            if e is not None:
+                e[4].record(stream)
+
+        for i in range(args.warmup):
+            train_step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            train_step(sets[i % len(sets)], ev[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        seg = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev]) * 1e3  # us
+        names = ["avq_assign_aggregate_kv" if fused else "avq_assign_aggregate", "avq_attention_fwd",
+                 "" if fused else "avq_assign_aggregate (V = K)", "avq_codebook_update"]
+        print(json.dumps({
+            "metric": "AVQ fwd + codebook update Mtokens/s", "unit": "Mtokens/s",
+            "value": round(cfg.B * cfg.N / (wall / args.steps) / 1e6, 3), "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+            "dtype": cfg.dtype, "data": "synthetic",
+            "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} M0={cfg.M0} C={cfg.C} "
+                                   f"P={P} block_q={cfg.block_q}; key sums {args.codebook_update}, decay 0.99"},
+            "calls_us": {n: round(float(seg[:, j].mean()), 2) for j, n in enumerate(names) if n}}), flush=True)
+        return
 
     if args.sweep:
         # one line: the whole pass at every refinement budget of the workload

@@ -96,6 +96,21 @@ int avq_assign_aggregate(const void* K, const void* V, const void* codebook,
                          void* stream);
 
 /*
+ * avq_assign_aggregate that also sums the keys per codeword, for the codebook
+ * update of the training recipe (App. A, Eq. 11): in the same pass,
+ *   ksum  out [B*H, Mt, d] float: sum of the keys of every codeword over the
+ *         same sets as vsum (parents their whole cell, children the keys that
+ *         moved to them),
+ * exactly what avq_assign_aggregate(K, K, ...) would write to its vsum, but
+ * without a second assignment pass and second read of the keys from HBM.
+ * ksum must not be NULL (AVQ_ERR_NULL) and must be 16-byte aligned; every
+ * other argument, output and error is that of avq_assign_aggregate.
+ */
+int avq_assign_aggregate_kv(const void* K, const void* V, const void* codebook, int B, int H,
+                            int N, int d, int M0, int C, int dtype, float* vsum,
+                            int32_t* counts, int32_t* assign, float* ksum, void* stream);
+
+/*
  * Bytes of device workspace avq_attention_fwd needs for these sizes (0 if the
  * sizes are invalid).  The workspace holds the value sums of every codeword
  * converted to the operand format of the weighted-value products; it is

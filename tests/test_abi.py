@@ -21,7 +21,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
-    assert set(names) == {"avq_assign_aggregate", "avq_attention_fwd", "avq_attention_fwd_approx",
+    assert set(names) == {"avq_assign_aggregate", "avq_assign_aggregate_kv", "avq_attention_fwd", "avq_attention_fwd_approx",
                           "avq_attention_fwd_ordered", "avq_attention_workspace_size", "avq_codebook_update",
                           "avq_status_string", "avq_version"}
     for n in names:
@@ -44,12 +44,15 @@ def _buf(n=64):
     return b, ctypes.c_void_p(addr)
 
 
-def _assign(L, **kw):
+def _call_assign(L, kv=False, **kw):
     _, p = _buf()
-    a = dict(K=p, V=p, cb=p, B=1, H=1, N=8, d=64, M0=4, C=2, dtype=1, vsum=p, counts=p, assign=None)
+    a = dict(K=p, V=p, cb=p, B=1, H=1, N=8, d=64, M0=4, C=2, dtype=1, vsum=p, counts=p, assign=None, ksum=p)
     a.update(kw)
-    return L.avq_assign_aggregate(a["K"], a["V"], a["cb"], a["B"], a["H"], a["N"], a["d"], a["M0"], a["C"],
-                                  a["dtype"], a["vsum"], a["counts"], a["assign"], None)
+    args = [a["K"], a["V"], a["cb"], a["B"], a["H"], a["N"], a["d"], a["M0"], a["C"], a["dtype"], a["vsum"],
+            a["counts"], a["assign"]]
+    if kv:
+        return L.avq_assign_aggregate_kv(*args, a["ksum"], None)
+    return L.avq_assign_aggregate(*args, None)
 
 
 def _call_attn(L, fn="avq_attention_fwd", **kw):
@@ -66,9 +69,13 @@ def _call_attn(L, fn="avq_attention_fwd", **kw):
                           a["ws"], a["wsb"], None)
 
 
-def test_assign_validation(L):
+@pytest.mark.parametrize("kv", [False, True])
+def test_assign_validation(L, kv):
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 4)
+
+    def _assign(L, **kw):  # both entry points validate the same way
+        return _call_assign(L, kv, **kw)
     assert _assign(L, dtype=7) == -3
     assert _assign(L, N=-1) == -2
     assert _assign(L, B=-1) == -2
@@ -85,6 +92,9 @@ def test_assign_validation(L):
     assert _assign(L, assign=mis) == -4
     assert _assign(L, B=0) == 0       # no (batch, head): nothing to do, nothing launched
     assert _assign(L, H=0, K=None) == 0
+    if kv:
+        assert _assign(L, ksum=None) == -1
+        assert _assign(L, ksum=mis) == -4
 
 
 @pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx", "avq_attention_fwd_ordered"])

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from adaptive_vector_quantized_amd import gen
-from parity_util import U32, say
+from parity_util import U32, check_vsum, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -93,10 +93,13 @@ def test_update_unit(name, decay):
     _close("codebook", gcb, ocb, np.abs(ocb).reshape(H, -1).max(1), 1e-6)
 
 
-def test_update_from_keys_grid64():
+@pytest.mark.parametrize("fused", [False, True])
+def test_update_from_keys_grid64(fused):
     """The whole step from the keys of the 64x64-grid workload (bf16 keys,
-    M0 = 64, C = 8, 12 heads): the aggregation call with V = K, then the update,
-    from a state of one key at every codeword's position."""
+    M0 = 64, C = 8, 4 heads, batch 2), from a state of one key at every
+    codeword's position: the key sums from the aggregation call with V = K, or
+    (fused) from avq_assign_aggregate_kv next to the value sums, then the
+    update."""
     import torch
     from adaptive_vector_quantized_amd import _lib
     cfg = gen.CONFIGS["grid64"].replace(B=2, H=4)
@@ -109,7 +112,12 @@ def test_update_from_keys_grid64():
     dev = torch.device("cuda:0")
     K = torch.from_numpy(data["K"]).to(torch.bfloat16).reshape(cfg.B, cfg.H, cfg.N, cfg.d).contiguous().to(dev)
     S, Nm, cb = (torch.from_numpy(a.copy()).to(dev) for a in (S0, N0, cb32))
-    _lib.update_codebook(K, cb, S, Nm, cfg.C, decay)
+    if fused:
+        V = torch.from_numpy(data["V"]).to(torch.bfloat16).reshape(K.shape).contiguous().to(dev)
+        _, counts_g, _, ksum_g = _lib.assign_aggregate_kv(K, V, cb.to(torch.bfloat16).contiguous(), cfg.C)
+        _lib.codebook_update(ksum_g, counts_g, S, Nm, cb, cfg.C, decay)
+    else:
+        _lib.update_codebook(K, cb, S, Nm, cfg.C, decay)
     torch.cuda.synchronize()
     gS, gN, gcb = S.cpu().numpy(), Nm.cpu().numpy(), cb.cpu().numpy()
     o = oracle.Oracle.for_cfg(cfg)
@@ -143,3 +151,31 @@ def test_update_from_keys_grid64():
     cerr = np.abs(kids_mean - gcb[:, :M0]).max()
     say(f"  constraint: max|mean(children) - parent| = {cerr:.2e}")
     assert cerr <= 64 * U32 * np.abs(gcb).max()
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}), ("grid64", {}), ("grid64", dict(d=128, H=2)),
+                                       ("grid64", dict(M0=256, C=0, P=0)), ("tiny", dict(N=1000, C=16))])
+def test_assign_aggregate_kv(name, over):
+    """avq_assign_aggregate_kv: assignments and counts exact, value sums and
+    key sums within the float32 summation bound of the oracle's sums."""
+    from adaptive_vector_quantized_amd import _lib
+    cfg = gen.CONFIGS[name].replace(**over)
+    data = gen.make(cfg, checker=oracle.MarginChecker())
+    say(f"[kv] {cfg.name} {over} B{cfg.B} H{cfg.H} N{cfg.N} d{cfg.d} M0{cfg.M0} C{cfg.C} {cfg.dtype}")
+    import torch
+    K = to_device(data["K"], cfg.dtype, cfg.B, cfg.H)
+    V = to_device(data["V"], cfg.dtype, cfg.B, cfg.H)
+    cb = torch.from_numpy(data["codebook"])
+    cb = (cb.to(torch.bfloat16) if cfg.dtype == "bf16" else cb).contiguous().cuda()
+    vsum, counts, assign, ksum = _lib.assign_aggregate_kv(K, V, cb, cfg.C, want_assign=True)
+    torch.cuda.synchronize()
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(assign.cpu().numpy().reshape(cfg.BH, cfg.N), row)
+    ov, oc = o.aggregate(data["V"], parent, row)
+    ok, _ = o.aggregate(data["K"], parent, row)
+    assert np.array_equal(counts.cpu().numpy().reshape(cfg.BH, cfg.Mt), oc)
+    vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
+    kabs, _ = o.aggregate(np.abs(data["K"].astype(np.float64)), parent, row)
+    check_vsum(vsum.cpu().numpy().reshape(cfg.BH, cfg.Mt, cfg.d), ov, vabs, oc)
+    check_vsum(ksum.cpu().numpy().reshape(cfg.BH, cfg.Mt, cfg.d), ok, kabs, oc)
