@@ -61,8 +61,8 @@ int assign_call(const void* K, const void* V, const void* codebook, int B, int H
   if (avq::assign_smem_bytes(dtype, d, M0, C) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
   const int64_t Mt = (int64_t)M0 * (1 + C);
   hipStream_t st = (hipStream_t)stream;
-  rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, counts, BH * Mt, st));
-  if (rc == AVQ_OK && with_keys) rc = from_hip(avq::launch_zero(ksum, BH * Mt * d, nullptr, 0, st));
+  rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, with_keys ? ksum : nullptr, with_keys ? BH * Mt * d : 0, counts,
+                                 BH * Mt, st));
   if (rc != AVQ_OK || N == 0) return rc;
   return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, vsum, counts, assign,
                                      with_keys ? ksum : nullptr, st));

@@ -526,10 +526,12 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(f32x4* __restrict__ a, int64_t na4, int* __restrict__ b, int64_t nb) {
+__global__ __launch_bounds__(256) void zero_kernel(f32x4* __restrict__ a, int64_t na4, f32x4* __restrict__ a2,
+                                                   int64_t na24, int* __restrict__ b, int64_t nb) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na4; i += stride) a[i] = z;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na24; i += stride) a2[i] = z;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nb; i += stride) b[i] = 0;
 }
 
@@ -588,12 +590,13 @@ static hipError_t launch_assign_w(const void* K, const void* V, const void* cb, 
   return launch_assign_t<T, D, 16, false>(K, V, cb, BH, H, N, M0, C, vsum, counts, assign, ksum, st);
 }
 
-hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st) {
-  const int64_t work = nv / 4 > nc ? nv / 4 : nc;
+hipError_t launch_zero(float* vsum, int64_t nv, float* ksum, int64_t nk, int* counts, int64_t nc, hipStream_t st) {
+  const int64_t work = std::max(std::max(nv / 4, nk / 4), nc);
   int64_t blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (f32x4*)vsum, nv / 4, counts, nc);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (f32x4*)vsum, nv / 4, (f32x4*)ksum, nk / 4,
+                     counts, nc);
   return hipGetLastError();
 }
 

@@ -25,7 +25,8 @@ struct AttnTraits {
   static constexpr int kChunkRows = 64;
 };
 
-hipError_t launch_zero(float* vsum, int64_t nv, int* counts, int64_t nc, hipStream_t st);
+// zeroes nv floats of vsum, nk floats of ksum (both multiples of 4) and nc ints of counts
+hipError_t launch_zero(float* vsum, int64_t nv, float* ksum, int64_t nk, int* counts, int64_t nc, hipStream_t st);
 hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
                          int C, float* vsum, int* counts, int* assign, float* ksum, hipStream_t st);
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH);
