@@ -20,7 +20,7 @@ int check_common(int B, int H, int N, int d, int M0, int C, int dtype) {
   if (B < 0 || H < 0 || N < 0) return AVQ_ERR_SHAPE;
   if (d < 1 || M0 < 1 || C < 0) return AVQ_ERR_SHAPE;
   if (d != 64 && d != 128) return AVQ_ERR_UNSUPPORTED;
-  if (M0 > 256 || C > 16) return AVQ_ERR_UNSUPPORTED;
+  if (M0 > 512 || C > 16) return AVQ_ERR_UNSUPPORTED;
   if ((int64_t)B * H > 65535) return AVQ_ERR_UNSUPPORTED;
   return AVQ_OK;
 }

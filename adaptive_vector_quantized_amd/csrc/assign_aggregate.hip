@@ -120,7 +120,7 @@ static AssignLds assign_lds(int es, int d, int M0, int C, int chunk, bool parent
   at[5] = o; o = al16(o + 8 * 4);                  // scan partials
   at[6] = o; o = al16(o + Mt * 2);                 // codeword -> slot
   at[7] = o; o = al16(o + Mt * 2);                 // slot -> codeword
-  at[8] = o; o = al16(o + (size_t)chunk * 2);      // parent << 8 | child slot of every key
+  at[8] = o; o = al16(o + (size_t)chunk * 2);      // parent << 5 | child slot of every key
   at[11] = o; o = al16(o + (size_t)chunk * 4);     // parent slot | child slot << 16 of every key
   at[10] = o;
   AssignLds L;
@@ -335,7 +335,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     if (hh ? kval[1] : kval[0]) {
       const bool moved = cs_ >= 0 && dc_ < db_;
       const int sl = moved ? 1 + cs_ : 0;
-      sBin[k_ - cstart] = (unsigned short)((a_ << 8) | sl);
+      sBin[k_ - cstart] = (unsigned short)((a_ << 5) | sl);  // sl <= C <= 16, a_ < 512
       atomicAdd(&sHist[a_ * (C + 1) + sl], 1);
       if (assign) assign[(int64_t)bh * N + k_] = moved ? M0 + a_ * C + cs_ : a_;
     }
@@ -359,16 +359,21 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   load_rows(Vb);
   lds_barrier();
 
-  // ---- slots: thread p owns parent p (M0 <= 256) and its C children -------
-  int nz = 0, pcount = 0;
-  if (tid < M0) {
+  // ---- slots: thread t owns parents t and t + 256 (M0 <= 512) and their C children
+  constexpr int kPPT = 2;  // parents per thread
+  int nz = 0, pcount[kPPT] = {0, 0};
+#pragma unroll
+  for (int k = 0; k < kPPT; ++k) {
+    const int par = tid + 256 * k;
+    if (par < M0) {
 #pragma unroll 1
-    for (int sl = 0; sl <= C; ++sl) {
-      const int c = sHist[tid * (C + 1) + sl];
-      pcount += c;
-      nz += (sl > 0 && c > 0);
+      for (int sl = 0; sl <= C; ++sl) {
+        const int c = sHist[par * (C + 1) + sl];
+        pcount[k] += c;
+        nz += (sl > 0 && c > 0);
+      }
+      nz += pcount[k] > 0;
     }
-    nz += pcount > 0;
   }
   const int incl = wave_incl_scan(nz, lane);
   if (lane == 63) sScan[wave] = incl;
@@ -380,15 +385,19 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     off += w < wave ? sScan[w] : 0;
     nslots += sScan[w];
   }
-  if (tid < M0 && pcount > 0) {
-    sSlot[tid] = (unsigned short)off;
-    sRow[off++] = (unsigned short)tid;
+#pragma unroll
+  for (int k = 0; k < kPPT; ++k) {
+    const int par = tid + 256 * k;
+    if (par < M0 && pcount[k] > 0) {
+      sSlot[par] = (unsigned short)off;
+      sRow[off++] = (unsigned short)par;
 #pragma unroll 1
-    for (int sl = 1; sl <= C; ++sl) {
-      if (sHist[tid * (C + 1) + sl] > 0) {
-        const int r = M0 + tid * C + sl - 1;
-        sSlot[r] = (unsigned short)off;
-        sRow[off++] = (unsigned short)r;
+      for (int sl = 1; sl <= C; ++sl) {
+        if (sHist[par * (C + 1) + sl] > 0) {
+          const int r = M0 + par * C + sl - 1;
+          sSlot[r] = (unsigned short)off;
+          sRow[off++] = (unsigned short)r;
+        }
       }
     }
   }
@@ -396,7 +405,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // slots of every key: parent slot | child slot << 16 (0xFFFF: the key stayed)
   for (int k = tid; k < nval; k += 256) {
     const int x = sBin[k];
-    const int p = x >> 8, sl = x & 255;
+    const int p = x >> 5, sl = x & 31;
     const uint32_t cs = sl ? (uint32_t)sSlot[M0 + p * C + sl - 1] : 0xFFFFu;
     sKS[k] = (uint32_t)sSlot[p] | (cs << 16);
   }
@@ -515,13 +524,21 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   }
 
   // ---- counts --------------------------------------------------------------
-  if (tid < M0 && pcount > 0) {
-    int* cnt = counts + (int64_t)bh * Mt;
-    atomicAdd(&cnt[tid], pcount);
+  // (from the histogram, still intact in LDS: no register stays live across
+  // the aggregation for them)
+  int* cnt = counts + (int64_t)bh * Mt;
+#pragma unroll
+  for (int k = 0; k < kPPT; ++k) {
+    const int par = tid + 256 * k;
+    if (par < M0) {
+      int total = 0;
 #pragma unroll 1
-    for (int sl = 1; sl <= C; ++sl) {
-      const int c = sHist[tid * (C + 1) + sl];
-      if (c) atomicAdd(&cnt[M0 + tid * C + sl - 1], c);
+      for (int sl = 0; sl <= C; ++sl) {
+        const int c = sHist[par * (C + 1) + sl];
+        total += c;
+        if (sl > 0 && c) atomicAdd(&cnt[M0 + par * C + sl - 1], c);
+      }
+      if (total) atomicAdd(&cnt[par], total);
     }
   }
 }

@@ -273,10 +273,11 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
 }
 
 // PL: the parents' codewords are held in LDS (M0 <= 64); else they are read
-// from L2 one block ahead of their MFMAs.  The parents' value fragments are
-// held in LDS too, except at d = 128 with more than 64 parents, where they are
-// read from L2 at their MFMAs (the LDS then holds two workgroups)
-template <class T, int D, int W, bool PL>
+// from L2 one block ahead of their MFMAs.  VL: the parents' value fragments
+// are held in LDS (always at d = 64); else they are read from L2 at their
+// MFMAs (at d = 128 beyond 64 parents, where the LDS then holds two
+// workgroups)
+template <class T, int D, int W, bool PL, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
     const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int nblkP = M0p / 32;
   const int Pp = P > 0 ? P : 1;
   constexpr bool parents_lds = PL;
-  constexpr bool values_lds = PL || D == 64;
+  constexpr bool values_lds = VL;
   frag_t* sPC = (frag_t*)smem;                                        // [nblkP*FA] if parents_lds
   pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV] if values_lds
   // the children's arrays exist only when P > 0, the importance partials only
@@ -322,8 +323,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   float* sW = sBc + nCH;                                              // [M0p][4] partials per wave
   int* sSel = (int*)(sW + (need_imp ? M0p * 4 : 0));                  // [nw][Pp]
   int* sFlag = sSel + nw * Pp;                                        // [2] all parents hold keys; chunk needs masks
-  float* sPass = (float*)(sFlag + 2);                                 // [4] keys of the parents of each 64-parent pass
-  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 8) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
+  float* sPass = (float*)(sFlag + 2);                                 // [8] keys of the parents of each 64-parent pass
+  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 12) - smem) + 15) & ~15));  // [nw][32][kYRow] output staging
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -609,30 +610,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         if (j < M0) sW[j * 4 + wave] = t[0] * nj;
       }
       lds_barrier();
-      // every wave forms the totals and its own copy of the selection
-      constexpr int MAXG = 4;  // up to 256 parents, one per lane per group
-      uint32_t u[MAXG];
-#pragma unroll
-      for (int g = 0; g < MAXG; ++g) {
-        const int j = g * 64 + lane;
-        float s = 0.0f;
-        if (g * 64 < M0) {  // j < M0p
-          const f32x4 p4 = *(const f32x4*)(sW + j * 4);
-          s = (p4[0] + p4[1]) + (p4[2] + p4[3]);
-          if (importance && wave == 0 && j < M0) importance[((int64_t)bh * ntiles + tile) * M0 + j] = s;
-        }
-        u[g] = __float_as_uint(s);  // 0 past M0: never above a threshold search candidate
-      }
+      // every wave forms the totals and its own copy of the selection; the
+      // importance of parent 64 g + lane as a bit pattern (0 past M0: never
+      // above a threshold search candidate), loaded for as many groups as the
+      // parents fill
+      auto imp_bits = [&](int g) -> uint32_t {
+        if (g * 64 >= M0) return 0u;
+        const f32x4 p4 = *(const f32x4*)(sW + (g * 64 + lane) * 4);  // j < M0p
+        return __float_as_uint((p4[0] + p4[1]) + (p4[2] + p4[3]));
+      };
+      if (importance && wave == 0)
+        for (int g = 0; g * 64 < M0; ++g)
+          if (g * 64 + lane < M0)
+            importance[((int64_t)bh * ntiles + tile) * M0 + g * 64 + lane] = __uint_as_float(imp_bits(g));
       if (P > 0) {
         int* gout = (topp && wave == 0) ? topp + ((int64_t)bh * ntiles + tile) * P : nullptr;
         if (parents_lds || M0 <= 64) {
-          uint32_t u1[1] = {u[0]};
+          uint32_t u1[1] = {imp_bits(0)};
           select_top<1>(u1, M0, P, lane, sSel + wave * Pp, gout);
         } else if (M0 <= 128) {
-          uint32_t u2[2] = {u[0], u[1]};
+          uint32_t u2[2] = {imp_bits(0), imp_bits(1)};
           select_top<2>(u2, M0, P, lane, sSel + wave * Pp, gout);
+        } else if (M0 <= 256) {
+          uint32_t u4[4] = {imp_bits(0), imp_bits(1), imp_bits(2), imp_bits(3)};
+          select_top<4>(u4, M0, P, lane, sSel + wave * Pp, gout);
         } else {
-          select_top<4>(u, M0, P, lane, sSel + wave * Pp, gout);
+          uint32_t u8[8];
+#pragma unroll
+          for (int g = 0; g < 8; ++g) u8[g] = imp_bits(g);
+          select_top<8>(u8, M0, P, lane, sSel + wave * Pp, gout);
         }
         __builtin_amdgcn_wave_barrier();
       } else {
@@ -809,7 +815,7 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   b += 2 * ch * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
   if (P > 0 || importance) b += M0p * 4 * 4;           // importance partials
-  b += nw * (size_t)(P > 0 ? P : 1) * 4 + 32; // selections, flags, keys per pass
+  b += nw * (size_t)(P > 0 ? P : 1) * 4 + 48; // selections, flags, keys per pass
   b = (b + 15) & ~(size_t)15;
   b += nw * 32 * kYRow * 4;                   // output staging
   return b;
@@ -833,7 +839,7 @@ int attention_tiles_per_wg(int BH, int N, int bq) {
   return (T + per_bh - 1) / per_bh;
 }
 
-template <class T, int D, int W, bool PL>
+template <class T, int D, int W, bool PL, bool VL>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, bool approx, const int* order, hipStream_t st) {
@@ -852,7 +858,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
     if (e != hipSuccess) return e;
   }
   const size_t smem = attention_smem_bytes(dtype, D, M0, C, P, bq, importance != nullptr);
-  auto kern = attention_kernel<T, D, W, PL>;
+  auto kern = attention_kernel<T, D, W, PL, VL>;
   hipError_t e = raise_lds_limit((const void*)kern, smem);
   if (e != hipSuccess) return e;
   const int tpw = attention_tiles_per_wg(BH, N, bq);
@@ -865,17 +871,28 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   return hipGetLastError();
 }
 
+template <class T, int D, int W>
+static hipError_t launch_attn_v(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
+                                int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
+                                void* ws, bool approx, const int* order, hipStream_t st) {
+  if (M0 <= 64)
+    return launch_attn_t<T, D, W, true, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
+                                              ws, approx, order, st);
+  // at d = 64 the values stay in LDS at every M0 (measured: at 512 flat codewords
+  // one LDS-resident workgroup per CU beats two reading the values from L2)
+  return launch_attn_t<T, D, W, false, D == 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp,
+                                                importance, ws, approx, order, st);
+}
+
 template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, bool approx, const int* order, hipStream_t st) {
-  const bool pl = M0 <= 64;
-  if (C <= 8) {
-    if (pl) return launch_attn_t<T, D, 8, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
-    return launch_attn_t<T, D, 8, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
-  }
-  if (pl) return launch_attn_t<T, D, 16, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
-  return launch_attn_t<T, D, 16, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+  if (C <= 8)
+    return launch_attn_v<T, D, 8>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx,
+                                  order, st);
+  return launch_attn_v<T, D, 16>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx,
+                                 order, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,

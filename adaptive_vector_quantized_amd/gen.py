@@ -98,6 +98,9 @@ CONFIGS = {
     # flat codebook of 256 codewords (no children, plain VQ attention) at the headline shape
     "flat256": Config("flat256", B=2, H=16, N=16384, d=64, M0=256, C=0, P=0, block_q=128,
                       dtype="bf16", grid=128, parents="zipf", seed=1005),
+    # flat codebook of 512 codewords at the headline shape (Tab. 2's largest flat VQ row)
+    "flat512": Config("flat512", B=2, H=16, N=16384, d=64, M0=512, C=0, P=0, block_q=128,
+                      dtype="bf16", grid=128, parents="zipf", seed=1006),
     # refinement-budget sweep on the 128x128 grid, one batch
     "sweep": Config("sweep", B=1, H=16, N=16384, d=64, M0=64, C=8, P=16, block_q=128,
                     dtype="bf16", grid=128, parents="zipf", seed=1004, sweep_P=(0, 4, 16, 64)),

@@ -33,7 +33,7 @@
  * dtype: AVQ_F32 (float) or AVQ_BF16 (bfloat16) for Q, K, V and the codebook.
  * Value sums, counts and outputs are float / int32 in both cases.
  *
- * Supported sizes: d in {64, 128}; 1 <= M0 <= 256; 0 <= C <= 16.  C = 0 is a
+ * Supported sizes: d in {64, 128}; 1 <= M0 <= 512; 0 <= C <= 16.  C = 0 is a
  * flat codebook of M0 codewords (plain VQ attention, the pages' fused flat-VQ
  * baseline of Sec. 5): keys are assigned to the nearest codeword only, and
  * the attention call then requires P = 0.

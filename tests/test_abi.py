@@ -82,7 +82,7 @@ def test_assign_validation(L, kv):
     assert _assign(L, C=-1) == -2
     assert _assign(L, M0=0) == -2
     assert _assign(L, d=96) == -5
-    assert _assign(L, M0=257) == -5
+    assert _assign(L, M0=513) == -5
     assert _assign(L, C=17) == -5
     assert _assign(L, K=None) == -1
     assert _assign(L, vsum=None) == -1

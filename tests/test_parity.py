@@ -107,7 +107,7 @@ def test_child_widths(C):
     _full_check(_data("grid64", C=C, H=2, N=1024 + 37, grid=None), 8)
 
 
-@pytest.mark.parametrize("M0,P", [(100, 20), (256, 32), (200, 0)])
+@pytest.mark.parametrize("M0,P", [(100, 20), (256, 32), (200, 0), (512, 48), (300, 300)])
 def test_tiled_parents(M0, P):
     # parents beyond one tile of 64: exact two-pass denominator
     _full_check(_data("grid64", M0=M0, H=2, N=2048 + 64 + 5, grid=None), P)
@@ -122,7 +122,7 @@ def test_tiled_parents_d128(dtype):
     _full_check(_data("grid64", d=128, M0=256, H=2, N=2048 + 64 + 5, grid=None, dtype=dtype), 32)
 
 
-@pytest.mark.parametrize("d,M0,P", [(64, 256, 32), (64, 100, 20), (128, 256, 32), (64, 64, 16)])
+@pytest.mark.parametrize("d,M0,P", [(64, 256, 32), (64, 100, 20), (128, 256, 32), (64, 64, 16), (64, 512, 64)])
 def test_approx_denominator(d, M0, P):
     """App. B (Eq. 13-14) through avq_attention_fwd_approx: importances per
     64-parent tile with the extrapolated denominator, against the oracle's;
@@ -256,7 +256,7 @@ def test_ordered_flat_codebook():
     _ordered_check(_place_along(data, order), 0, order)
 
 
-@pytest.mark.parametrize("M0", [64, 256])
+@pytest.mark.parametrize("M0", [64, 256, 512])
 def test_flat_codebook(M0):
     """C = 0: a flat codebook of M0 codewords, plain VQ attention (P = 0)."""
     _full_check(_data("grid64", M0=M0, C=0, P=0), 0)
