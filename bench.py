@@ -91,25 +91,54 @@ def load_traffic(call: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, P):
-    """The oracle as it stands, on the host cores: assignment, aggregation,
-    importance, top-P and the substituted-codebook output for the whole
-    workload (one run; OpenMP over the B*H heads)."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, P, runs: int = 3):
+    """The oracle as it stands, on the host cores, over the whole workload
+    (OpenMP over the B*H heads): the assignment and aggregation, then the
+    importance, top-P and substituted-codebook output, each timed separately;
+    the median of `runs` passes."""
     import oracle
     from adaptive_vector_quantized_amd import gen
     data = gen.make(cfg)
     o = oracle.Oracle.for_cfg(cfg)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    t0 = time.perf_counter()
-    o.forward(data["Q"], data["K"], data["V"], data["codebook"], P, cfg.block_q, cfg.scale)
-    dt = time.perf_counter() - t0
+    t_k1, t_k2 = [], []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        parent, row = o.assign(data["K"], data["codebook"])
+        vsum, counts = o.aggregate(data["V"], parent, row)
+        t1 = time.perf_counter()
+        w = o.importance(data["Q"], data["codebook"], counts, cfg.block_q, cfg.scale)
+        sel = o.select(w, P)
+        o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel, P, cfg.block_q, cfg.scale)
+        t2 = time.perf_counter()
+        t_k1.append(t1 - t0)
+        t_k2.append(t2 - t1)
+    k1, k2 = float(np.median(t_k1)), float(np.median(t_k2))
+    dt = k1 + k2
     return {
         "value": cfg.B * cfg.N / dt / 1e6,
         "unit": "Mtokens/s",
         "cores": min(threads, cfg.BH),
         "kind": "oracle",
-        "sample": f"the whole workload ({cfg.B}x{cfg.H} heads x {cfg.N} tokens), one pass of the plain-C oracle "
-                  f"(assign, aggregate, importance, top-P, substituted-codebook output): {dt:.2f} s",
+        "sample": f"the whole workload ({cfg.B}x{cfg.H} heads x {cfg.N} tokens), plain-C oracle, median of {runs} "
+                  f"passes: assign + aggregate {k1:.3f} s, importance + top-P + substituted-codebook output "
+                  f"{k2:.3f} s",
+        "assign_aggregate_s": round(k1, 4),
+        "attention_s": round(k2, 4),
+        "cpu_model": _cpu_model(),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+        "nproc": os.cpu_count(),
     }
 
 
@@ -340,6 +369,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "gpu_span_ms_per_step": round(gpu_span / max(1, args.steps - 1) * 1e3, 5),
+        "Mhead_tokens_per_s": round(cfg.B * cfg.H * cfg.N / (wall / args.steps) / 1e6, 3),
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
