@@ -128,6 +128,44 @@ def pin_counts_and_sums(lib):
         assert counts[0, p] - kids[0, p].sum() == (truth == p).sum()
 
 
+def pin_key_order(lib):
+    """Alg. 1 treats keys independently: permuting the keys (with their
+    values) permutes the assignments the same way and leaves every count and
+    value sum unchanged."""
+    cfg = gen.CONFIGS["tiny"]
+    data = gen.make(cfg)
+    o = _O(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C)
+    parent, row = o.assign(data["K"], data["codebook"])
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    perm = np.random.default_rng(9).permutation(cfg.N)
+    Kp, Vp = data["K"][:, perm], data["V"][:, perm]
+    parent_p, row_p = o.assign(Kp, data["codebook"])
+    assert np.array_equal(parent_p, parent[:, perm]) and np.array_equal(row_p, row[:, perm])
+    vsum_p, counts_p = o.aggregate(Vp, parent_p, row_p)
+    assert np.array_equal(counts_p, counts)
+    np.testing.assert_allclose(vsum_p, vsum, rtol=1e-13, atol=1e-12)
+
+
+def pin_aggregate_segments(lib):
+    """Eq. 3 as histograms and segment sums of the assignment, formed with
+    numpy: a parent's count and value sum cover every key whose parent it is,
+    a child's the keys whose final row it is."""
+    cfg, data = _small_case(53, N=300, d=6, M0=5, C=3)
+    o = _O(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C)
+    parent, row = o.assign(data["K"], data["codebook"])
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    V = data["V"].astype(np.float64)
+    for bh in range(cfg.BH):
+        n = np.bincount(parent[bh], minlength=cfg.Mt)
+        moved = row[bh] >= cfg.M0
+        n += np.bincount(row[bh][moved], minlength=cfg.Mt)
+        assert np.array_equal(counts[bh], n)
+        s = np.zeros((cfg.Mt, cfg.d))
+        np.add.at(s, parent[bh], V[bh])
+        np.add.at(s, row[bh][moved], V[bh][moved])
+        np.testing.assert_allclose(vsum[bh], s, rtol=1e-13, atol=1e-12)
+
+
 # ---------------------------------------------------------------- importance
 def pin_importance_closed_form(lib):
     """Eq. 7 on a case computed by hand: two parents, one query, logits a and
@@ -685,6 +723,8 @@ PINS = {
     "assign_ties": pin_assign_ties,
     "assign_brute_force": pin_assign_brute_force,
     "counts_and_sums": pin_counts_and_sums,
+    "key_order": pin_key_order,
+    "aggregate_segments": pin_aggregate_segments,
     "importance_closed_form": pin_importance_closed_form,
     "importance_properties": pin_importance_properties,
     "select": pin_select,
