@@ -27,7 +27,7 @@ def to_device(a: np.ndarray, dtype: str, B: int, H: int):
 
 
 def run_gpu(data: dict, P: int, want_assign=True, want_topp=True, want_importance=True, bq=None,
-            approx=False, order=None, y_fill=None):
+            approx=False, order=None, y_fill=None, scale=None):
     """Both kernels through the C interface; returns numpy arrays shaped like the oracle's."""
     import torch
     from adaptive_vector_quantized_amd import _lib
@@ -44,7 +44,7 @@ def run_gpu(data: dict, P: int, want_assign=True, want_topp=True, want_importanc
     Y = None
     if y_fill is not None:
         Y = torch.full((B, H, cfg.N, cfg.d), float(y_fill), dtype=torch.float32, device=Q.device)
-    Y, topp, imp = _lib.attention_fwd(Q, cb, vsum, counts, cfg.C, P, bq, cfg.scale,
+    Y, topp, imp = _lib.attention_fwd(Q, cb, vsum, counts, cfg.C, P, bq, cfg.scale if scale is None else scale,
                                       want_topp=want_topp and P > 0, want_importance=want_importance,
                                       approx_denominator=approx, query_order=qo, Y=Y)
     torch.cuda.synchronize()

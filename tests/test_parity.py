@@ -319,3 +319,70 @@ def test_full_size_grid128_gilbert():
         assert np.array_equal(g["sel"][bh, t], sel[0, 0]), (bh, t)
         Y = os_.attention_substituted(Qt, cbh, vsum[bh:bh + 1], counts[bh:bh + 1], sel, cfg.P, bq, cfg.scale)
         compare_y(g["Y"][bh:bh + 1, rows], Y, cfg.dtype, f"grid128 Gilbert bh{bh} tile{t}")
+
+
+
+def _decisive_check(data, P, scale, where):
+    """Inputs not drawn with top-P margins: assignments and counts exact, the
+    importances within 1e-5 * |tile|, the top-P sets equal on the tiles whose
+    P-th and (P+1)-th importances are 1e-4 apart (relative), and Y for the
+    GPU's own sets against the substituted-codebook form."""
+    cfg = data["cfg"]
+    bq = cfg.block_q
+    say(f"[parity] {where}: {cfg.name} N{cfg.N} d{cfg.d} M0{cfg.M0} C{cfg.C} P{P} {cfg.dtype} scale {scale:g}")
+    g = run_gpu(data, P, scale=scale)
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    assert np.array_equal(g["row"], row)
+    vsum, counts = o.aggregate(data["V"], parent, row)
+    assert np.array_equal(g["counts"], counts)
+    vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
+    check_vsum(g["vsum"], vsum, vabs, counts)
+    w = o.importance(data["Q"], data["codebook"], counts, bq, scale)
+    w64 = o.importance_f64(data["Q"], data["codebook"], counts, bq, scale)
+    werr = np.abs(g["importance"].astype(np.float64) - w64).max()
+    say(f"  importance max|err| = {werr:.3e}")
+    assert werr <= 1e-5 * bq
+    if P > 0:
+        srt = -np.sort(-w64, axis=-1)
+        margin = (srt[..., P - 1] - srt[..., P]) / np.maximum(srt[..., P - 1], 1.0)
+        decisive = (margin >= 1e-4) | ((srt[..., P - 1] == 0.0) & (srt[..., P] == 0.0))
+        sel = o.select(w, P)
+        say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
+        assert np.array_equal(g["sel"][decisive], sel[decisive])
+        sel = g["sel"]
+    else:
+        sel = np.zeros((cfg.BH, (cfg.N + bq - 1) // bq, 0), np.int32)
+    Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel, P, bq, scale)
+    compare_y(g["Y"], Y, cfg.dtype, where)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale_mult", [8.0, 30.0])
+def test_large_logits(dtype, scale_mult):
+    """Logits far from zero (the logit scale raised 8x and 30x: logit spreads
+    of hundreds): the stabiliser is raised lazily, by more than 2^8 at a time,
+    so the fp16 weight operand stays in [0, 2^8] and no exponential
+    overflows; the output still matches."""
+    data = _data("grid64", dtype=dtype, H=2, N=2048 + 64 + 5, grid=None)
+    _decisive_check(data, data["cfg"].P, data["cfg"].scale * scale_mult, f"large logits x{scale_mult:g} {dtype}")
+
+
+@pytest.mark.parametrize("vmult", [1e-6, 3e4])
+def test_value_magnitude(vmult):
+    """Values far from unit size (1e-6 and 3e4 times the generator's): the
+    value sums go to the fp16 operand through a power-of-two scale per
+    (batch, head), so neither underflow nor overflow reaches the output."""
+    base = _data("grid64", H=2, N=2048 + 64 + 5, grid=None)
+    cfg = base["cfg"]
+    data = dict(base, V=gen.round_to_dtype(base["V"].astype(np.float64) * vmult, cfg.dtype))
+    _decisive_check(data, cfg.P, cfg.scale, f"values x{vmult:g}")
+
+
+@pytest.mark.parametrize("N", [1, 37, 127])
+def test_short_sequences(N):
+    """Fewer queries than one tile (one partial tile; a single token)."""
+    cfg = gen.CONFIGS["grid64"].replace(N=N, grid=None, H=3)
+    data = gen.make(cfg, checker=oracle.MarginChecker())
+    P = min(cfg.P, cfg.M0)
+    _decisive_check(data, P, cfg.scale, f"N={N}")
