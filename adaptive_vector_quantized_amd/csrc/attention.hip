@@ -272,11 +272,11 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   }
 }
 
-// PL: the parents' codewords are held in LDS (M0 <= 64); else they are read
-// from L2 one block ahead of their MFMAs.  VL: the parents' value fragments
-// are held in LDS (always at d = 64); else they are read from L2 at their
-// MFMAs (at d = 128 beyond 64 parents, where the LDS then holds two
-// workgroups)
+// PL: the parents' codewords are all held in LDS (M0 <= 64); else they pass
+// through a one-pass (64-parent) LDS buffer that the workgroup's waves share.
+// VL: the parents' value fragments are held in LDS (d = 64 up to 256
+// parents); else they are read from L2 at their MFMAs (at d = 128 beyond 64
+// parents and at d = 64 beyond 256, where the LDS then holds two workgroups)
 template <class T, int D, int W, bool PL, bool VL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_kernel(
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
@@ -308,8 +308,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int Pp = P > 0 ? P : 1;
   constexpr bool parents_lds = PL;
   constexpr bool values_lds = VL;
-  frag_t* sPC = (frag_t*)smem;                                        // [nblkP*FA] if parents_lds
-  pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 0));  // [nblkP*FV] if values_lds
+  frag_t* sPC = (frag_t*)smem;                                        // [nblkP*FA] if parents_lds, else one pass [2*FA]
+  pvfrag_t* sPV = (pvfrag_t*)(sPC + (parents_lds ? nblkP * FA : 2 * FA));  // [nblkP*FV] if values_lds
   // the children's arrays exist only when P > 0, the importance partials only
   // when importances are formed
   const bool need_imp = (P > 0) || (importance != nullptr);
@@ -443,6 +443,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
   };
 
+  // One pass of 64 parents' codeword fragments in LDS when they are not all
+  // held there: every wave copies its share (global -> LDS, no registers);
+  // wait_pass makes the whole pass visible, release_pass (after the pass's
+  // logits) lets the buffer be refilled -- with the next pass, or the first
+  // pass again for the second (importance) pass or the next tile -- while
+  // the rest of the pass runs.
+  auto stage_pass = [&](int pt2) {
+    for (int u = wave; u < 2 * KS; u += nw) {
+      const int b = u / KS, s = u % KS;
+      const int j = pt2 * 64 + b * 32 + ql;
+      lds_dma<BA>(cbh + (int64_t)(j < M0 ? j : 0) * D + s * 2 * E + E * hh, sPC + u * 64);
+    }
+  };
+  auto wait_pass = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  auto release_pass = [&](int next) {
+    lds_barrier();
+    if (next >= 0) stage_pass(next);
+  };
+  if constexpr (!parents_lds) stage_pass(0);
+
   // ---- query tiles ------------------------------------------------------------
   for (int tile = tile0; tile < tile1; ++tile) {
     const bool qv = qrow >= 0;
@@ -472,36 +495,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     f32x16 lg[2];
 
     // parents (Alg. 2, the pass over the parent codewords), 64 per pass (the padding rows past M0 have
-    // count 0 and logit -inf); parents not held in LDS are read from L2 one
-    // 32-row block ahead of their MFMAs
-    frag_t pa[parents_lds ? 1 : KS];
-    auto load_parents = [&](int bb) {
-      if constexpr (!parents_lds) {
-        const int j = bb * 32 + ql;
-        const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) pa[s] = *(const frag_t*)(ap + s * 2 * E);
-      }
-    };
-    if constexpr (!parents_lds) load_parents(0);
+    // count 0 and logit -inf); parents not all held in LDS pass through a
+    // one-pass LDS buffer shared by the workgroup's waves (staged_pass)
+    const bool second_pass = need_imp && !approx && !parents_lds;
     for (int pt = 0; pt < nPT; ++pt) {
       const int j0 = pt * 64;
+      if constexpr (!parents_lds) wait_pass();
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int bb = pt * 2 + b;
+        const int bb = parents_lds ? pt * 2 + b : b;
         lg[b] = zero16();
-        if constexpr (parents_lds) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
-        } else {
-          frag_t cur[KS];
-#pragma unroll
-          for (int s = 0; s < KS; ++s) cur[s] = pa[s];
-          if (bb + 1 < nblkP) load_parents(bb + 1);
-#pragma unroll
-          for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(cur[s], qf[s], lg[b]);
-        }
+        for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
       }
+      if constexpr (!parents_lds)
+        release_pass(pt + 1 < nPT ? pt + 1 : (second_pass || tile + 1 < tile1) ? 0 : -1);
       if (!all_parents || j0 + 64 > M0) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -587,19 +595,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * rz;
         } else {
           // second pass with the final stabiliser and denominator (exact Z of Eq. 7)
+          wait_pass();
+          f32x16 l2[2];
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            f32x16 l2 = zero16();
-            const int j = j0 + 32 * b + ql;
-            const in_t* ap = cbh + (int64_t)(j < M0 ? j : 0) * D + E * hh;
+            l2[b] = zero16();
 #pragma unroll
-            for (int s = 0; s < KS; ++s) l2 = T::mma_in(*(const frag_t*)(ap + s * 2 * E), qf[s], l2);
+            for (int s = 0; s < KS; ++s) l2[b] = T::mma_in(sPC[(b * KS + s) * 64 + lane], qf[s], l2[b]);
+          }
+          release_pass(pt + 1 < nPT ? pt + 1 : tile + 1 < tile1 ? 0 : -1);
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float n = sNp[j0 + b * 32 + col_of(r, hh)];
-              t[b * 16 + r] = n > 0.0f ? fast_exp2(fmaf(l2[r], sl2, -m)) * n * rz : 0.0f;
+              t[b * 16 + r] = n > 0.0f ? fast_exp2(fmaf(l2[b][r], sl2, -m)) * n * rz : 0.0f;
             }
-          }
         }
         // one pass: the count n_j of Eq. 7 is a factor of the whole sum over
         // the tile's queries, applied once after the reduction (the second
@@ -810,8 +821,8 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   const size_t CH = d == 64 ? AttnTraits<64>::kChunkRows : AttnTraits<128>::kChunkRows;
   (void)C;
   const size_t ch = P > 0 ? CH : 0;
-  size_t b = (M0p <= 64 ? M0p * d * es : 0);  // parents' codeword fragments
-  if (M0p <= 64 || d == 64) b += M0p * d * es;  // parents' value fragments (else read from L2)
+  size_t b = (M0p <= 64 ? M0p : 64) * d * es;  // parents' codeword fragments (all, or one 64-parent pass)
+  if (M0p <= 64 || (d == 64 && M0p <= 256)) b += M0p * d * es;  // parents' value fragments (else read from L2)
   b += 2 * ch * d * es;                       // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
   if (P > 0 || importance) b += M0p * 4 * 4;           // importance partials
@@ -878,10 +889,17 @@ static hipError_t launch_attn_v(const void* Q, const void* cb, const float* vsum
   if (M0 <= 64)
     return launch_attn_t<T, D, W, true, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
                                               ws, approx, order, st);
-  // at d = 64 the values stay in LDS at every M0 (measured: at 512 flat codewords
-  // one LDS-resident workgroup per CU beats two reading the values from L2)
-  return launch_attn_t<T, D, W, false, D == 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp,
-                                                importance, ws, approx, order, st);
+  // at d = 64 the values stay in LDS up to 256 parents; beyond, LDS-resident
+  // values would leave one workgroup per CU, with nothing to cover the
+  // staged parent passes' barriers (measured at 512 flat codewords: 211 us
+  // against 177 us reading the values from L2 with two workgroups per CU)
+  if constexpr (D == 64) {
+    if (M0 <= 256)
+      return launch_attn_t<T, D, W, false, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp,
+                                                 importance, ws, approx, order, st);
+  }
+  return launch_attn_t<T, D, W, false, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
+                                              ws, approx, order, st);
 }
 
 template <class T, int D>
