@@ -82,7 +82,7 @@ __device__ __forceinline__ float frag_sumsq(typename T::frag_t v, float acc) {
 
 // LDS layout of one workgroup (byte offsets; every array 16-byte aligned)
 struct AssignLds {
-  unsigned par, norm, cn, list, hist, scan, slot, row, bin, ks, acc, total;
+  unsigned par, norm, cn, list, stage, hist, scan, slot, row, bin, ks, acc, total;
 };
 
 static size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -106,12 +106,13 @@ static AssignLds assign_lds(int es, int d, int M0, int C, int chunk, bool parent
   const size_t Mt = (size_t)M0 * (1 + C);
   const size_t NB = (size_t)M0 * (C + 1);
   const size_t ldp = d + 16 / es;
-  size_t o = 0, at[12];
+  size_t o = 0, at[13];
   // assignment phase only
   at[0] = o; o = al16(o + (parents_lds ? M0p * ldp * es : 0));  // parents, padded rows
   at[1] = o; o = al16(o + M0p * 4);                // parent norms
   at[2] = o; o = al16(o + 4 * 32 * 4);             // child-block norms, per wave
   at[3] = o; o = al16(o + 4 * 64 * 4);             // distinct parents of a wave step
+  at[12] = o; o = al16(o + (parents_lds ? 0 : (size_t)64 * d * es));  // one 64-parent pass (from L2)
   // aggregation phase only: four partial value tiles (up to 64 columns) over
   // the same bytes
   at[9] = 0;
@@ -125,6 +126,7 @@ static AssignLds assign_lds(int es, int d, int M0, int C, int chunk, bool parent
   at[10] = o;
   AssignLds L;
   L.par = (unsigned)at[0]; L.norm = (unsigned)at[1]; L.cn = (unsigned)at[2]; L.list = (unsigned)at[3];
+  L.stage = (unsigned)at[12];
   L.hist = (unsigned)at[4]; L.scan = (unsigned)at[5]; L.slot = (unsigned)at[6]; L.row = (unsigned)at[7];
   L.bin = (unsigned)at[8]; L.ks = (unsigned)at[11]; L.acc = (unsigned)at[9]; L.total = (unsigned)at[10];
   return L;
@@ -206,9 +208,28 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   const int srow = 2 * (rr / W) + hr, crow = rr % W;  // slot and child of this lane's A row
   int* list = sList + wave * 64;
   float* cn = sCN + wave * 32;
+  // Parents read from L2 pass through LDS 64 at a time, one copy shared by
+  // the four waves (instead of each wave reading every parent from L2): each
+  // wave copies its share global -> LDS; the whole pass is visible after a
+  // wait and a barrier; after the pass's MFMAs a barrier frees the buffer for
+  // the next pass (or the first one of the next step).  Every wave then runs
+  // every step and pass, a wave past the end of the keys with all of its keys
+  // masked, so that all of them reach every barrier.
+  frag_t* sPS = (frag_t*)(smem + L.stage);
+  const int npass = (nblkP + 1) / 2;
+  auto stage_pass = [&](int ps) {
+    for (int u = wave; u < 2 * KS; u += 4) {
+      const int b = u / KS, s = u % KS;
+      const int prow = min(ps * 64 + b * 32 + ql, M0 - 1);
+      lds_dma<(int)sizeof(frag_t)>(cbh + (int64_t)prow * D + s * 2 * E + E * hh, sPS + u * 64);
+    }
+  };
+  if constexpr (!PL) stage_pass(0);
   for (int it = 0; it < KPW; it += 64) {
     const int kloc = wave * KPW + it;  // first key of the step, chunk-relative
-    if (kloc >= nval) break;
+    if constexpr (PL) {
+      if (kloc >= nval) break;
+    }
     frag_t kf[2][KS];
     int key[2];
     bool kval[2];
@@ -223,14 +244,11 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     // nearest parent: first minimum of ||c||^2 - 2 k.c
     float best[2] = {INFINITY, INFINITY};
     int bidx[2] = {0, 0};
-    for (int blk = 0; blk < nblkP; ++blk) {
+    auto parent_block = [&](int blk, auto frag_at) {
       f32x16 a0 = zero16(), a1 = zero16();
-      // rows past M0 (norm +inf) are never chosen; from L2 they repeat row M0 - 1
-      const in_t* ap = PL ? sPar + (blk * 32 + ql) * LDP + E * hh
-                          : cbh + (int64_t)min(blk * 32 + ql, M0 - 1) * D + E * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        frag_t a = *(const frag_t*)(ap + s * 2 * E);
+        const frag_t a = frag_at(s);
         a0 = T::mma_in(a, kf[0][s], a0);
         a1 = T::mma_in(a, kf[1][s], a1);
       }
@@ -242,6 +260,26 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
         const float d1 = nrm - 2.0f * a1[r];
         if (d0 < best[0]) { best[0] = d0; bidx[0] = row; }
         if (d1 < best[1]) { best[1] = d1; bidx[1] = row; }
+      }
+    };
+    if constexpr (PL) {
+      for (int blk = 0; blk < nblkP; ++blk) {
+        const in_t* ap = sPar + (blk * 32 + ql) * LDP + E * hh;
+        parent_block(blk, [&](int s) { return *(const frag_t*)(ap + s * 2 * E); });
+      }
+    } else {
+      // rows past M0 (norm +inf) are never chosen; they repeat row M0 - 1
+      for (int ps = 0; ps < npass; ++ps) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int blk = ps * 2 + b;
+          if (blk < nblkP) parent_block(blk, [&](int s) { return sPS[(b * KS + s) * 64 + lane]; });
+        }
+        lds_barrier();
+        const int next = ps + 1 < npass ? ps + 1 : (it + 64 < KPW ? 0 : -1);
+        if (next >= 0) stage_pass(next);
       }
     }
 #pragma unroll

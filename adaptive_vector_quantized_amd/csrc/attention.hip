@@ -90,11 +90,9 @@ __device__ __forceinline__ int parent_of_col(int c) {
   return 32 * (c >> 5) + row_of(r_of_col(q), h_of_col(q));
 }
 
-// asynchronous copy of BYTES per lane from global memory into LDS at
-// lds_base + lane * BYTES (lds_base must be the same for the whole wave)
-// The same through a buffer descriptor (base and size in scalar registers,
-// a 32-bit byte offset per lane): a fragment at or past the descriptor's size
-// reads as zeros.
+// lds_dma (avq_device.h) through a buffer descriptor (base and size in scalar
+// registers, a 32-bit byte offset per lane): a fragment at or past the
+// descriptor's size reads as zeros.
 constexpr int kBufWord3 = 0x00020000;     // word 3 of a raw gfx9-family descriptor
 constexpr int kOutOfRange = 0x7FFFFFF0;   // a byte offset past any descriptor here
 template <int BYTES>
@@ -104,14 +102,6 @@ __device__ __forceinline__ void lds_dma_buf(__amdgpu_buffer_rsrc_t rs, int voff,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
   else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 4, voff, 0, 0, 0);
-}
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const void* gptr, void* lds_base) {
-  static_assert(BYTES == 16 || BYTES == 4, "fragment size");
-  if constexpr (BYTES == 16)
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-  else
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
 // Top-P of Alg. 2 over the importances one wave holds (parent j = 64 g + lane

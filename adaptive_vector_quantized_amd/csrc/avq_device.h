@@ -175,4 +175,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Global -> LDS copy of one fragment per lane (no registers): lane l's BYTES
+// at gptr land at lds_base + l * BYTES.  Counted by vmcnt; readers wait for it
+// and, across waves, for a barrier.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* gptr, void* lds_base) {
+  static_assert(BYTES == 16 || BYTES == 4, "fragment size");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
 }  // namespace avq
