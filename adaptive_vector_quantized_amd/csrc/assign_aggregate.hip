@@ -6,9 +6,10 @@
 // head).  Design for CDNA4:
 //   * Parent distances ||c||^2 - 2 k.c come from MFMA: parents of the head
 //     are staged once in LDS as the A operand (their norms are reduced from
-//     LDS; a large codebook is read from L2 instead when that fits more
-//     workgroups on a CU), keys are streamed from HBM straight into B-operand
-//     registers (64 keys per wave step) and stay there for the child search.
+//     LDS; a large codebook passes through LDS 64 parents at a time instead,
+//     when that fits more workgroups on a CU), keys are streamed from HBM
+//     straight into B-operand registers (64 keys per wave step) and stay
+//     there for the child search.
 //   * Child distances: the distinct parents of the wave's 64 keys are packed
 //     S = 32 / W at a time into a 32-row block of their children, one MFMA
 //     block per group; the children's norms come from the same operand
@@ -95,12 +96,12 @@ struct AssignShape {
   static constexpr int kChunk = 4 * KPW;         // keys per workgroup
   static constexpr int LDP = D + 16 / (int)sizeof(typename T::in_t);  // padded LDS row of a parent
   static constexpr int ACC_D = D < 64 ? D : 64;  // value columns per pass of the partial tiles
-  // waves per SIMD the registers are set for: parents in LDS, or read from L2
+  // waves per SIMD the registers are set for: the whole codebook in LDS, or 64 parents at a time
   static constexpr int kWavesLds = (D == 64 && T::E > 1) ? 4 : 2;
   static constexpr int kWavesL2 = T::E > 1 ? (D == 64 ? 4 : 3) : (D == 64 ? 3 : 2);
 };
 
-// parents_lds: the parents' codewords are staged in LDS (else read from L2)
+// parents_lds: all the parents' codewords are staged in LDS (else 64 at a time)
 static AssignLds assign_lds(int es, int d, int M0, int C, int chunk, bool parents_lds) {
   const size_t M0p = (M0 + 31) & ~31;
   const size_t Mt = (size_t)M0 * (1 + C);
@@ -133,8 +134,9 @@ static AssignLds assign_lds(int es, int d, int M0, int C, int chunk, bool parent
 }
 
 // W: width of a child slot in accumulator registers (C <= W, W in {4,8,16}).
-// PL: parents' codewords staged in LDS; else read from L2 by the MFMA loop
-// (large codebooks: the LDS then holds more workgroups per CU).
+// PL: all parents' codewords staged in LDS; else they pass through a shared
+// 64-parent LDS buffer (large codebooks: the LDS then holds more workgroups
+// per CU).
 template <class T, int D, int W, bool PL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PL ? AssignShape<T, D>::kWavesLds
                                                                           : AssignShape<T, D>::kWavesL2))) void

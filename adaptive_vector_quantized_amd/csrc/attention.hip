@@ -15,8 +15,10 @@
 //  2. attention_kernel.  A workgroup owns a contiguous range of query tiles
 //     of one (batch, head); one wave handles 32 queries of a tile.  The
 //     parents' codeword and value fragments are copied into LDS once per
-//     workgroup (up to 64 parents; beyond, the codewords, and at d = 128 also
-//     the value fragments, are read from L2); per tile, the selected
+//     workgroup (up to 64 parents; beyond, the codewords pass through a
+//     64-parent LDS buffer shared by the workgroup's waves, and the value
+//     fragments are read from L2 at d = 128 and at d = 64 beyond 256
+//     parents); per tile, the selected
 //     parents' children are copied into LDS by asynchronous buffer loads (no
 //     registers held, one wait).  The output goes out in streaming stores.
 //
