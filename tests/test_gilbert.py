@@ -92,3 +92,19 @@ def test_fig3_tiles_are_compact(bq, ntiles):
     # a square of n cells has a bounding perimeter of 4 sqrt(n)
     assert perimeter(tiles) < perimeter(raster)
     assert perimeter(tiles[:-1]) <= 1.3 * 4 * np.sqrt(bq)
+
+
+def test_every_small_grid():
+    """Every grid up to 32 x 32: a permutation of the cells, ending on the
+    starting edge of the long side, with unit steps except at most one diagonal
+    step, which occurs only when the long side is odd and the short one even."""
+    for W in range(1, 33):
+        for H in range(1, 33):
+            c = gilbert.curve(W, H)
+            assert len(c) == W * H and len(set(c)) == W * H, (W, H)
+            steps = np.abs(np.diff(np.array(c), axis=0)).sum(axis=1) if len(c) > 1 else np.zeros(0)
+            diag = int((steps == 2).sum())
+            assert (steps >= 1).all() and (steps <= 2).all(), (W, H)
+            long_, short = max(W, H), min(W, H)
+            assert diag <= (1 if long_ % 2 == 1 and short % 2 == 0 else 0), (W, H, diag)
+            assert (c[-1][1] == 0) if W >= H else (c[-1][0] == 0), (W, H)
