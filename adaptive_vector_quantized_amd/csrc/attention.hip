@@ -826,14 +826,14 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
 
 // Query tiles per workgroup: aim for about two resident workgroups per CU.
 int attention_tiles_per_wg(int BH, int N, int bq) {
-  static int cus = 0;
-  if (cus == 0) {
+  // CU count of the device, read once (a function-local static is initialised
+  // once even under concurrent first calls)
+  static const int cus = [] {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
+      return v;
+    return 256;
+  }();
   const int T = (N + bq - 1) / bq;
   const int target = 2 * cus;
   int per_bh = (target + BH - 1) / (BH > 0 ? BH : 1);
