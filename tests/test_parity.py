@@ -386,3 +386,29 @@ def test_short_sequences(N):
     data = gen.make(cfg, checker=oracle.MarginChecker())
     P = min(cfg.P, cfg.M0)
     _decisive_check(data, P, cfg.scale, f"N={N}")
+
+
+@pytest.mark.parametrize("approx", [False, True])
+def test_ordered_d128_tiled(approx):
+    """The ordered entry on the d = 128 path with 256 parents (the parents'
+    codewords through the shared one-pass buffer, values from L2), along the
+    Gilbert curve of the 64x64 grid; exact and App. B importances."""
+    data = _data("grid64", d=128, M0=256, P=32, H=2)
+    order = gilbert.query_order(64, 64)
+    _ordered_check(_place_along(data, order), 32, order, approx=approx)
+
+
+def test_ordered_block32():
+    """One wave per tile (block_q = 32) in Gilbert order."""
+    data = _data("grid64", block_q=32, H=3)
+    order = gilbert.query_order(64, 64)
+    _ordered_check(_place_along(data, order), data["cfg"].P, order)
+
+
+@pytest.mark.parametrize("N", [1, 100])
+def test_short_sequences_tiled(N):
+    """Fewer queries than one tile on the 256-parent d = 128 path (the shared
+    parent buffer with a single, partial tile per workgroup)."""
+    cfg = gen.CONFIGS["grid64"].replace(N=N, grid=None, H=2, d=128, M0=256, P=32)
+    data = gen.make(cfg, checker=oracle.MarginChecker())
+    _decisive_check(data, 32, cfg.scale, f"N={N} d128 M0=256")

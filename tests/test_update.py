@@ -179,3 +179,34 @@ def test_assign_aggregate_kv(name, over):
     kabs, _ = o.aggregate(np.abs(data["K"].astype(np.float64)), parent, row)
     check_vsum(vsum.cpu().numpy().reshape(cfg.BH, cfg.Mt, cfg.d), ov, vabs, oc)
     check_vsum(ksum.cpu().numpy().reshape(cfg.BH, cfg.Mt, cfg.d), ok, kabs, oc)
+
+
+
+def test_update_from_keys_d128_fused():
+    """The fused key sums at d = 128 with 256 parents (the assign kernel's
+    shared parent buffer), then the update, against the oracle."""
+    import torch
+    from adaptive_vector_quantized_amd import _lib
+    cfg = gen.CONFIGS["grid64"].replace(B=1, H=2, d=128, M0=256, N=2048 + 64 + 5, grid=None)
+    data = gen.make(cfg, checker=oracle.MarginChecker())
+    decay = 0.9
+    say(f"[update] from keys d128 M0 256 fused")
+    cb32 = data["codebook"].astype(np.float32)
+    S0, N0 = cb32.copy(), np.ones((cfg.H, cfg.Mt), np.float32)
+    dev = torch.device("cuda:0")
+    K = torch.from_numpy(data["K"]).to(torch.bfloat16).reshape(cfg.B, cfg.H, cfg.N, cfg.d).contiguous().to(dev)
+    V = torch.from_numpy(data["V"]).to(torch.bfloat16).reshape(K.shape).contiguous().to(dev)
+    S, Nm, cb = (torch.from_numpy(a.copy()).to(dev) for a in (S0, N0, cb32))
+    _, counts_g, _, ksum_g = _lib.assign_aggregate_kv(K, V, cb.to(torch.bfloat16).contiguous(), cfg.C)
+    _lib.codebook_update(ksum_g, counts_g, S, Nm, cb, cfg.C, decay)
+    torch.cuda.synchronize()
+    o = oracle.Oracle.for_cfg(cfg)
+    parent, row = o.assign(data["K"], data["codebook"])
+    ksum, counts = o.aggregate(data["K"], parent, row)
+    assert np.array_equal(counts_g.cpu().numpy().reshape(cfg.BH, cfg.Mt), counts)
+    oS, oN, ocb = o.codebook_update(ksum, counts, float(np.float32(decay)), S0, N0, cb32)
+    scale = np.abs(ocb).max()
+    err = np.abs(cb.cpu().numpy() - ocb).max() / scale
+    say(f"  codebook max err / max|C| = {err:.2e}")
+    assert err <= 1e-5
+    assert np.abs(Nm.cpu().numpy() - oN).max() <= 4 * U32 * (np.abs(oN).max() + 1.0)
