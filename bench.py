@@ -142,6 +142,85 @@ def cpu_baseline(cfg, P, runs: int = 3):
     }
 
 
+def complexity(args):
+    """Both calls over N in {4096, 16384, 65536} (B = 2, H = 16, d = 64, bf16) for flat
+    codebooks of M in {64, 128, 256, 512} (P = 0) and a hierarchical one (M0 = 64, C = 8,
+    P in {4, 16, 64}; and M0 = 128, P = 16): the median event time of each call over the timed
+    steps, against the codewords a key is compared with (M, or M0 + C) and the codewords a query
+    attends to (M, or M0 + P C).  Queries and values are seeded N(0, 1) draws on the device; a
+    codebook from the generator; keys are a codeword plus noise, one codeword per run of 64
+    consecutive tokens (the locality of the image workloads' 8x8 patches), or per token with
+    --complexity-order random.  One JSON line with every point and the log-log slopes."""
+    import torch
+    from adaptive_vector_quantized_amd import _lib, gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B, H, d = 2, 16, 64
+    steps = max(20, min(args.steps, 200))
+    warm = max(5, min(args.warmup, 50))
+    shapes = [("vq", M, 0, 0) for M in (64, 128, 256, 512)] + [("avq", 64, 8, P) for P in (4, 16, 64)] + \
+             [("avq", 128, 8, 16)]
+    rows = []
+    stream = torch.cuda.current_stream(dev)
+    for N in (4096, 16384, 65536):
+        g = torch.Generator(device=dev)
+        g.manual_seed(2000 + N)
+        Q, K, V = (torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16).contiguous()
+                   for _ in range(3))
+        for kind, M0, C, P in shapes:
+            cb = torch.from_numpy(gen.make_codebook(3000 + M0 + C, H, M0, C, d)).to(torch.bfloat16).contiguous().to(dev)
+            Mt = M0 * (1 + C)
+            vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
+            counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
+            Y = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+            ws = torch.empty(_lib.workspace_size(B, H, d, M0, C, torch.bfloat16), dtype=torch.uint8, device=dev)
+            run = 1 if args.complexity_order == "random" else 64
+            idx = torch.randint(0, Mt, (B, H, N // run), generator=g, device=dev).repeat_interleave(run, dim=2)
+            Kc = (cb.float()[torch.arange(H, device=dev)[None, :, None], idx] + 0.1 * K.float()).to(torch.bfloat16)
+            Kc = Kc.contiguous()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+            for i in range(warm + steps):
+                e = ev[i - warm] if i >= warm else None
+                if e:
+                    e[0].record(stream)
+                _lib.assign_aggregate(Kc, V, cb, C, vsum=vsum, counts=counts)
+                if e:
+                    e[1].record(stream)
+                _lib.attention_fwd(Q, cb, vsum, counts, C, P, 128, 1.0 / d ** 0.5, Y=Y, workspace=ws)
+                if e:
+                    e[2].record(stream)
+            torch.cuda.synchronize()
+            k1 = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+            k2 = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+            rows.append({"N": N, "kind": kind, "M0": M0, "C": C, "P": P, "precompute_codes": M0 + C,
+                         "attention_codes": M0 + P * C, "assign_aggregate_us": round(k1, 2),
+                         "attention_fwd_us": round(k2, 2)})
+            print(f"[bench] {rows[-1]}", file=sys.stderr, flush=True)
+            del cb, vsum, counts, Y, ws, Kc
+        del Q, K, V
+        torch.cuda.empty_cache()
+
+    def slope(xs, ys):
+        return float(np.polyfit(np.log(xs), np.log(ys), 1)[0])
+    fits = {}
+    for col, codes in (("assign_aggregate_us", "precompute_codes"), ("attention_fwd_us", "attention_codes")):
+        byN = [slope([r["N"] for r in rows if (r["kind"], r["M0"], r["P"]) == key], [r[col] for r in rows if (r["kind"], r["M0"], r["P"]) == key])
+               for key in {(r["kind"], r["M0"], r["P"]) for r in rows}]
+        vq = [r for r in rows if r["kind"] == "vq" and r["N"] == 65536]
+        fits[col] = {"slope_in_N": [round(x, 3) for x in sorted(byN)],
+                     "slope_in_codes_flat_N65536": round(slope([r[codes] for r in vq], [r[col] for r in vq]), 3)}
+        if col == "attention_fwd_us":
+            avq = [r for r in rows if r["kind"] == "avq" and r["M0"] == 64 and r["N"] == 65536]
+            fits[col]["slope_in_codes_avq_N65536"] = round(slope([r[codes] for r in avq], [r[col] for r in avq]), 3)
+    print(json.dumps({"metric": "call time versus N and codewords used (Tab. 1, Fig. 6)", "unit": "us",
+                      "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+                      "config": {"workload": "B=2 H=16 d=64 block_q=128, N in {4096, 16384, 65536}; flat M in "
+                                             "{64,128,256,512}; M0=64 C=8 P in {4,16,64}; M0=128 C=8 P=16; keys "
+                                             + ("drawn per token" if args.complexity_order == "random"
+                                                else "drawn per run of 64 tokens")},
+                      "steps": steps, "warmup": warm, "points": rows, "fits": fits}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +239,11 @@ def main():
                     help="time the forward pass plus the codebook update of the training recipe (App. A): key sums "
                          "from avq_assign_aggregate_kv (fused) or from a second aggregation call with V = K "
                          "(separate), then avq_codebook_update")
+    ap.add_argument("--complexity", action="store_true",
+                    help="time both calls over N and the number of codewords used (flat and hierarchical "
+                         "codebooks), with log-log slopes: the linear-scaling check of Tab. 1 / Fig. 6")
+    ap.add_argument("--complexity-order", choices=("runs", "random"), default="runs",
+                    help="key order of the complexity scan: one codeword per run of 64 tokens, or per token")
     ap.add_argument("--sweep", action="store_true",
                     help="time the whole pass at every refinement budget of the workload (e.g. --workload sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -175,6 +259,9 @@ def main():
     import torch
     from adaptive_vector_quantized_amd import _lib, gen, gilbert
 
+    if args.complexity:
+        complexity(args)
+        return
     cfg = gen.CONFIGS[args.workload]
     P = cfg.P if args.P is None else args.P
     dev = torch.device("cuda:0")
