@@ -94,3 +94,31 @@ def sub_problem(data: dict, bh: int, t: int):
     cfg = data["cfg"]
     i0, i1 = t * cfg.block_q, min(cfg.N, (t + 1) * cfg.block_q)
     return data["Q"][bh:bh + 1, i0:i1], i0, i1
+
+
+def run_attention_variants(data: dict, P: int, variants):
+    """Kernel 1 once, then kernel 2 once per variant (keyword arguments of
+    attention_fwd) on the same value sums and counts: the attention call is
+    deterministic, so variants that must agree can be compared bit for bit
+    (two runs of kernel 1 may round the value sums differently: they are
+    float atomics added in any order)."""
+    import torch
+    from adaptive_vector_quantized_amd import _lib
+    cfg = data["cfg"]
+    K = to_device(data["K"], cfg.dtype, cfg.B, cfg.H)
+    V = to_device(data["V"], cfg.dtype, cfg.B, cfg.H)
+    Q = to_device(data["Q"], cfg.dtype, cfg.B, cfg.H)
+    cb = torch.from_numpy(data["codebook"])
+    cb = (cb.to(torch.bfloat16) if cfg.dtype == "bf16" else cb).contiguous().cuda()
+    vsum, counts, _ = _lib.assign_aggregate(K, V, cb, cfg.C)
+    outs = []
+    for kw in variants:
+        kw = dict(kw)
+        if kw.get("query_order") is not None:
+            kw["query_order"] = torch.from_numpy(np.ascontiguousarray(kw["query_order"], dtype=np.int32)).cuda()
+        Y, topp, imp = _lib.attention_fwd(Q, cb, vsum, counts, cfg.C, P, cfg.block_q, cfg.scale,
+                                          want_topp=P > 0, want_importance=True, **kw)
+        torch.cuda.synchronize()
+        outs.append({"Y": Y.cpu().numpy(), "sel": None if topp is None else topp.cpu().numpy(),
+                     "importance": imp.cpu().numpy()})
+    return outs

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from adaptive_vector_quantized_amd import gen, gilbert
-from parity_util import check_vsum, compare_y, run_gpu, say, sub_problem
+from parity_util import check_vsum, compare_y, run_attention_variants, run_gpu, say, sub_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -154,8 +154,10 @@ def test_approx_denominator(d, M0, P):
     Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, g["sel"], P, bq, cfg.scale)
     compare_y(g["Y"], Y, cfg.dtype, f"approx d{d} M0{M0} P{P}")
     if M0 <= 64:
-        g0 = run_gpu(data, P)
-        assert np.array_equal(g["Y"], g0["Y"]) and np.array_equal(g["sel"], g0["sel"])
+        # one tile: the same call as avq_attention_fwd, on the same value sums
+        a, e = run_attention_variants(data, P, [dict(approx_denominator=True), {}])
+        assert np.array_equal(a["Y"], e["Y"]) and np.array_equal(a["sel"], e["sel"])
+        assert np.array_equal(a["importance"], e["importance"])
 
 
 def _place_along(data, order):
@@ -243,8 +245,7 @@ def test_ordered_identity_is_plain():
     data = _data("grid64", N=2048 + 64 + 5, grid=None, H=2)
     P = data["cfg"].P
     say("[parity] identity order against the plain call")
-    g0 = run_gpu(data, P)
-    g1 = run_gpu(data, P, order=np.arange(data["cfg"].N, dtype=np.int32))
+    g0, g1 = run_attention_variants(data, P, [{}, dict(query_order=np.arange(data["cfg"].N, dtype=np.int32))])
     for k in ("Y", "sel", "importance"):
         assert np.array_equal(g0[k], g1[k]), k
 
