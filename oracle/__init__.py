@@ -3,7 +3,8 @@
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The HIP library never does, and nothing
 here imports the HIP library.  The arithmetic lives in ``avq_oracle.c`` (plain
-loops, double precision for outputs); this file only marshals numpy arrays.
+loops, double precision throughout, decisions included); this file only
+marshals numpy arrays.
 """
 from __future__ import annotations
 
@@ -41,7 +42,6 @@ def load(path: Optional[str] = None):
     lib.avqo_assign.argtypes = [i32] * 6 + [P, P, P, P]
     lib.avqo_aggregate.argtypes = [i32] * 6 + [P, P, P, P, P]
     lib.avqo_importance.argtypes = [i32] * 6 + [P, P, P, i32, dbl, P]
-    lib.avqo_importance_f64.argtypes = [i32] * 6 + [P, P, P, i32, dbl, P]
     lib.avqo_importance_tiled_f64.argtypes = [i32] * 6 + [P, P, P, i32, dbl, i32, P]
     lib.avqo_select.argtypes = [i64, i32, i32, P, P]
     for f in (lib.avqo_attention_alg2, lib.avqo_attention_substituted):
@@ -112,17 +112,11 @@ class Oracle:
         _ok(self.lib.avqo_aggregate(*self.dims, _p(V), _p(parent), _p(row), _p(vsum), _p(counts)))
         return vsum, counts
 
-    # Eq. 7 (float decisions)
+    # Eq. 7, in double
     def importance(self, Q, codebook, counts, bq: int, scale: float):
         Q, cb, counts = _f64(Q), _f64(codebook), _i32(counts)
-        w = np.zeros((self.B * self.H, self.tiles(bq), self.M0), np.float32)
-        _ok(self.lib.avqo_importance(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, _p(w)))
-        return w
-
-    def importance_f64(self, Q, codebook, counts, bq: int, scale: float):
-        Q, cb, counts = _f64(Q), _f64(codebook), _i32(counts)
         w = np.zeros((self.B * self.H, self.tiles(bq), self.M0), np.float64)
-        _ok(self.lib.avqo_importance_f64(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, _p(w)))
+        _ok(self.lib.avqo_importance(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, _p(w)))
         return w
 
     def importance_tiled_f64(self, Q, codebook, counts, bq: int, scale: float, tile: int):
@@ -133,9 +127,9 @@ class Oracle:
         _ok(self.lib.avqo_importance_tiled_f64(*self.dims, _p(Q), _p(cb), _p(counts), bq, scale, tile, _p(w)))
         return w
 
-    # Alg. 2, the top-P parent choice
+    # Alg. 2, the top-P parent choice (on double importances)
     def select(self, w, P: int):
-        w = np.ascontiguousarray(w, dtype=np.float32)
+        w = _f64(w)
         R = int(np.prod(w.shape[:-1]))
         sel = np.zeros(w.shape[:-1] + (P,), np.int32)
         _ok(self.lib.avqo_select(R, self.M0, P, _p(w), _p(sel)))

@@ -10,13 +10,14 @@
  * equation and algorithm.  Every function is written for a reader checking it
  * against the paper by eye: plain loops, no blocking, no fusion.
  *
- * Precision.  Outputs (value sums, attention outputs) are computed in double.
- * The two places where floating point decides an integer -- the nearest
- * codeword (Sec. 4.2, Alg. 1) and the top-P parent choice (Eq. 7, Alg. 2) --
- * are taken in single precision, the precision the GPU kernels decide in; the
- * paper fixes no precision for them.  Separate double-precision functions
- * report how far each decision is from a tie (used to draw inputs whose
- * decisions do not depend on rounding).
+ * Precision.  Everything is computed in double on the inputs widened
+ * exactly (bf16 and fp32 values are exact doubles): the value sums, the
+ * attention outputs, and the two places where floating point decides an
+ * integer -- the nearest codeword (Sec. 4.2, Alg. 1) and the top-P parent
+ * choice (Eq. 7, Alg. 2).  The paper fixes no precision; double is the
+ * plainest reading of "the exact result".  Separate functions report how far
+ * each decision is from a tie (used to draw inputs whose decisions do not
+ * depend on the rounding of any implementation).
  *
  * Layouts (all row-major, contiguous):
  *   K, V, Q    [B*H][N][d]      token rows of head h of batch b at bh = b*H + h
@@ -32,7 +33,7 @@
  *   avqo_assign               generator ground truth, keys equal to codewords,
  *                             hand-built ties, brute force on small inputs
  *   avqo_aggregate            column sums, parent/child count relations
- *   avqo_importance(_f64)     two-parent closed form; w >= 0, w = 0 iff n = 0,
+ *   avqo_importance           two-parent closed form; w >= 0, w = 0 iff n = 0,
  *                             sum of w over a tile = its query count
  *   avqo_importance_tiled_f64 first codeword tile holds |I| * N_seen / N of the
  *                             mass; one-codeword tiles: w_0 = |I| n_0 / N; the
@@ -73,12 +74,11 @@ static int ntiles(int N, int bq) { return (N + bq - 1) / bq; }
  * closer than the best child so far; the key moves to the best child only when
  * that child is strictly closer than the parent.
  * Outputs: parent[bh*N + j] = chosen parent row; row[bh*N + j] = final row
- * (the child row if the key moved, else the parent row).
- * Decision arithmetic in float (see header). */
-static float dist2_f32(const double* k, const double* c, int d) {
-    float acc = 0.0f;
+ * (the child row if the key moved, else the parent row). */
+static double dist2(const double* k, const double* c, int d) {
+    double acc = 0.0;
     for (int t = 0; t < d; ++t) {
-        float diff = (float)k[t] - (float)c[t];
+        double diff = k[t] - c[t];
         acc += diff * diff;
     }
     return acc;
@@ -96,16 +96,16 @@ int avqo_assign(int B, int H, int N, int d, int M0, int C,
         for (int j = 0; j < N; ++j) {
             const double* k = K + ((int64_t)bh * N + j) * d;
             int a = 0;
-            float dbest = dist2_f32(k, cbh, d);
+            double dbest = dist2(k, cbh, d);
             for (int m = 1; m < M0; ++m) {
-                float dm = dist2_f32(k, cbh + (int64_t)m * d, d);
+                double dm = dist2(k, cbh + (int64_t)m * d, d);
                 if (dm < dbest) { dbest = dm; a = m; }
             }
             int64_t c0 = M0 + (int64_t)a * C;
-            float dchild = INFINITY;
+            double dchild = INFINITY;
             int64_t cstar = c0;
             for (int c = 0; c < C; ++c) {
-                float dc = dist2_f32(k, cbh + (c0 + c) * d, d);
+                double dc = dist2(k, cbh + (c0 + c) * d, d);
                 if (dc < dchild) { dchild = dc; cstar = c0 + c; }
             }
             parent[(int64_t)bh * N + j] = a;
@@ -146,44 +146,54 @@ int avqo_aggregate(int B, int H, int N, int d, int M0, int C,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Eq. 7 with Alg. 2 (the parent pass and the importance): importance of every parent for every query tile.
+/* Eq. 7 with Alg. 2 (the parent pass and the importance), one query tile:
+ * importance w[M0] of the parents for the queries Qt[nq][d]:
  *   s_ij = scale * Q_i . C_j over the parents j,
  *   m_i  = max of s_ij over the parents with n_j > 0 (Eq. 18),
  *   A_ij = exp(s_ij - m_i), set to zero where n_j = 0 (Sec. D),
  *   Z_i  = sum_j A_ij n_j,
  *   w_j  = sum_{i in tile} A_ij n_j / Z_i.
- * Decision arithmetic in float (see header).  w: [BH][T][M0]. */
+ * s: scratch of M0 doubles. */
+static double dotd(const double* a, const double* b, int d) {
+    double acc = 0.0;
+    for (int t = 0; t < d; ++t) acc += a[t] * b[t];
+    return acc;
+}
+
+static void importance_tile(int nq, int d, int M0, const double* Qt, const double* cbh,
+                            const int32_t* n, double scale, double* s, double* w) {
+    for (int j = 0; j < M0; ++j) w[j] = 0.0;
+    for (int i = 0; i < nq; ++i) {
+        const double* q = Qt + (int64_t)i * d;
+        double m = -INFINITY;
+        for (int j = 0; j < M0; ++j) {
+            s[j] = scale * dotd(q, cbh + (int64_t)j * d, d);
+            if (n[j] > 0 && s[j] > m) m = s[j];
+        }
+        double Z = 0.0;
+        for (int j = 0; j < M0; ++j)
+            if (n[j] > 0) Z += exp(s[j] - m) * n[j];
+        for (int j = 0; j < M0; ++j)
+            if (n[j] > 0) w[j] += exp(s[j] - m) * n[j] / Z;
+    }
+}
+
+/* Eq. 7 for every query tile of every (batch, head): w [BH][T][M0]. */
 int avqo_importance(int B, int H, int N, int d, int M0, int C,
                     const double* Q, const double* cb, const int32_t* counts,
-                    int bq, double scale, float* w) {
+                    int bq, double scale, double* w) {
     if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 0 || bq < 1) return ORACLE_ERR;
     const int64_t Mt = mt_of(M0, C);
     const int BH = B * H, T = ntiles(N, bq);
 #pragma omp parallel for schedule(static)
     for (int bh = 0; bh < BH; ++bh) {
         const int h = bh % H;
-        const double* cbh = cb + (int64_t)h * Mt * d;
-        const int32_t* n = counts + (int64_t)bh * Mt;
-        float* s = (float*)malloc(sizeof(float) * M0);
+        double* s = (double*)malloc(sizeof(double) * M0);
         for (int t = 0; t < T; ++t) {
-            float* wt = w + ((int64_t)bh * T + t) * M0;
-            for (int j = 0; j < M0; ++j) wt[j] = 0.0f;
-            const int i_end = (t + 1) * bq < N ? (t + 1) * bq : N;
-            for (int i = t * bq; i < i_end; ++i) {
-                const double* q = Q + ((int64_t)bh * N + i) * d;
-                float m = -INFINITY;
-                for (int j = 0; j < M0; ++j) {
-                    float acc = 0.0f;
-                    for (int u = 0; u < d; ++u) acc += (float)q[u] * (float)cbh[(int64_t)j * d + u];
-                    s[j] = (float)scale * acc;
-                    if (n[j] > 0 && s[j] > m) m = s[j];
-                }
-                float Z = 0.0f;
-                for (int j = 0; j < M0; ++j)
-                    if (n[j] > 0) Z += expf(s[j] - m) * (float)n[j];
-                for (int j = 0; j < M0; ++j)
-                    if (n[j] > 0) wt[j] += expf(s[j] - m) * (float)n[j] / Z;
-            }
+            const int i0 = t * bq, i1 = (t + 1) * bq < N ? (t + 1) * bq : N;
+            importance_tile(i1 - i0, d, M0, Q + ((int64_t)bh * N + i0) * d,
+                            cb + (int64_t)h * Mt * d, counts + (int64_t)bh * Mt, scale, s,
+                            w + ((int64_t)bh * T + t) * M0);
         }
         free(s);
     }
@@ -193,10 +203,10 @@ int avqo_importance(int B, int H, int N, int d, int M0, int C,
 /* Alg. 2, the parent choice: the P parents of largest importance.  Equal importances are
  * ordered by the lower parent index.  The chosen set is written ascending.
  * w: [R][M0] (R = BH*T rows), sel: [R][P]. */
-int avqo_select(int64_t R, int M0, int P, const float* w, int32_t* sel) {
+int avqo_select(int64_t R, int M0, int P, const double* w, int32_t* sel) {
     if (P < 0 || P > M0) return ORACLE_ERR;
     for (int64_t r = 0; r < R; ++r) {
-        const float* wr = w + r * M0;
+        const double* wr = w + r * M0;
         int32_t* out = sel + r * P;
         int k = 0;
         /* parent j is chosen iff fewer than P parents precede it in the order
@@ -213,13 +223,7 @@ int avqo_select(int64_t R, int M0, int P, const float* w, int32_t* sel) {
 }
 
 /* ------------------------------------------------------------------------ */
-/* helpers for the output forms */
-static double dotd(const double* a, const double* b, int d) {
-    double acc = 0.0;
-    for (int t = 0; t < d; ++t) acc += a[t] * b[t];
-    return acc;
-}
-
+/* helper for the output forms */
 static int in_sel(const int32_t* sel, int P, int p) {
     for (int k = 0; k < P; ++k) if (sel[k] == p) return 1;
     return 0;
@@ -459,12 +463,6 @@ int avqo_exact_attention(int BH, int N, int d, const double* Q, const double* K,
  * summation order, and the comparison rules decide such a tie; those pairs
  * are left out (e.g. with C = 1, Eq. 5 makes the only child equal its
  * parent). */
-static double dist2_f64(const double* k, const double* c, int d) {
-    double acc = 0.0;
-    for (int t = 0; t < d; ++t) { double diff = k[t] - c[t]; acc += diff * diff; }
-    return acc;
-}
-
 static int same_vec(const double* a, const double* b, int d) {
     for (int t = 0; t < d; ++t) if (a[t] != b[t]) return 0;
     return 1;
@@ -485,7 +483,7 @@ int avqo_key_margins(int B, int H, int N, int d, int M0, int C,
             double b1 = INFINITY, b2 = INFINITY;
             int a = -1, a2 = -1;
             for (int m = 0; m < M0; ++m) {
-                double dm = dist2_f64(k, cbh + (int64_t)m * d, d);
+                double dm = dist2(k, cbh + (int64_t)m * d, d);
                 if (dm < b1) { b2 = b1; a2 = a; b1 = dm; a = m; }
                 else if (dm < b2) { b2 = dm; a2 = m; }
             }
@@ -497,7 +495,7 @@ int avqo_key_margins(int B, int H, int N, int d, int M0, int C,
                 int i1 = -1, i2 = -1;
                 for (int c = 0; c < C; ++c) {
                     const int64_t rowc = M0 + (int64_t)a * C + c;
-                    double dc = dist2_f64(k, cbh + rowc * d, d);
+                    double dc = dist2(k, cbh + rowc * d, d);
                     if (dc < c1) { c2 = c1; i2 = i1; c1 = dc; i1 = (int)rowc; }
                     else if (dc < c2) { c2 = dc; i2 = (int)rowc; }
                 }
@@ -516,24 +514,6 @@ int avqo_key_margins(int B, int H, int N, int d, int M0, int C,
     return ORACLE_OK;
 }
 
-/* Eq. 7 in double, one query tile: importance w[M0] of the parents for the
- * queries Qt[nq][d] (same steps as avqo_importance). */
-static void importance_tile_f64(int nq, int d, int M0, const double* Qt, const double* cbh,
-                                const int32_t* n, double scale, double* s, double* w) {
-    for (int j = 0; j < M0; ++j) w[j] = 0.0;
-    for (int i = 0; i < nq; ++i) {
-        const double* q = Qt + (int64_t)i * d;
-        double m = -INFINITY;
-        for (int j = 0; j < M0; ++j) {
-            s[j] = scale * dotd(q, cbh + (int64_t)j * d, d);
-            if (n[j] > 0 && s[j] > m) m = s[j];
-        }
-        double Z = 0.0;
-        for (int j = 0; j < M0; ++j) if (n[j] > 0) Z += exp(s[j] - m) * n[j];
-        for (int j = 0; j < M0; ++j) if (n[j] > 0) w[j] += exp(s[j] - m) * n[j] / Z;
-    }
-}
-
 /* Gap of the top-P choice of one tile, in double: with the importances sorted
  * in decreasing order w(1) >= w(2) >= ..., returns
  * (w(P) - w(P+1)) / max(1, w(P)) when 0 < P < M0 and w(P+1) > 0, else inf
@@ -544,7 +524,7 @@ double avqo_tile_margin(int nq, int d, int M0, const double* Qt, const double* c
     if (P <= 0 || P >= M0 || nq <= 0) return INFINITY;
     double* s = (double*)malloc(sizeof(double) * M0);
     double* w = (double*)malloc(sizeof(double) * M0);
-    importance_tile_f64(nq, d, M0, Qt, cbh, n, scale, s, w);
+    importance_tile(nq, d, M0, Qt, cbh, n, scale, s, w);
     /* P-th and (P+1)-th largest by selection */
     double wp = 0.0, wq = 0.0;
     for (int j = 0; j < M0; ++j) {
@@ -571,28 +551,6 @@ int avqo_tile_margins(int B, int H, int N, int d, int M0, int C,
         const int i0 = t * bq, i1 = (t + 1) * bq < N ? (t + 1) * bq : N;
         out[r] = avqo_tile_margin(i1 - i0, d, M0, Q + ((int64_t)bh * N + i0) * d,
                                   cb + (int64_t)h * Mt * d, counts + (int64_t)bh * Mt, P, scale);
-    }
-    return ORACLE_OK;
-}
-
-/* importance in double for every tile (reporting; same layout as avqo_importance) */
-int avqo_importance_f64(int B, int H, int N, int d, int M0, int C,
-                        const double* Q, const double* cb, const int32_t* counts,
-                        int bq, double scale, double* w) {
-    if (B < 0 || H < 0 || N < 0 || d < 1 || M0 < 1 || C < 0 || bq < 1) return ORACLE_ERR;
-    const int64_t Mt = mt_of(M0, C);
-    const int BH = B * H, T = ntiles(N, bq);
-#pragma omp parallel for schedule(static)
-    for (int bh = 0; bh < BH; ++bh) {
-        const int h = bh % H;
-        double* s = (double*)malloc(sizeof(double) * M0);
-        for (int t = 0; t < T; ++t) {
-            const int i0 = t * bq, i1 = (t + 1) * bq < N ? (t + 1) * bq : N;
-            importance_tile_f64(i1 - i0, d, M0, Q + ((int64_t)bh * N + i0) * d,
-                                cb + (int64_t)h * Mt * d, counts + (int64_t)bh * Mt, scale, s,
-                                w + ((int64_t)bh * T + t) * M0);
-        }
-        free(s);
     }
     return ORACLE_OK;
 }

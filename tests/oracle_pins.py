@@ -84,6 +84,26 @@ def pin_assign_ties(lib):
     assert row[0].tolist() == [0, 1, 1, 5, 2, 3, 3]
 
 
+def pin_assign_exact_arithmetic(lib):
+    """Eq. 2's arg min is taken on the exact squared distances: two distances
+    that differ by less than single precision resolves (2^24 against
+    2^24 + 1/2 + 2^-28, and 2^24 against 2^24 - 1/2 + 2^-28) are still ordered
+    correctly, so the nearer parent wins although it has the higher index, and
+    a child nearer than its parent by that little still takes the key (Alg. 1).
+    One dimension; every coordinate and squared distance is exact in double."""
+    e = 2.0 ** -14
+    o = _O(lib, 1, 1, 1, 1, 2, 1)
+    K = np.zeros((1, 1, 1))
+    # parent choice: parent 1 at 4096 beats parent 0 at -(4096 + e)
+    cb = np.array([[[-(4096.0 + e)], [4096.0], [-1e5], [1e5]]])
+    parent, row = o.assign(K, cb)
+    assert parent.tolist() == [[1]] and row.tolist() == [[1]]
+    # move decision: the child at -(4096 - e) is nearer than its parent at 4096
+    cb = np.array([[[4096.0], [1e5], [-(4096.0 - e)], [-1e5]]])
+    parent, row = o.assign(K, cb)
+    assert parent.tolist() == [[0]] and row.tolist() == [[2]]
+
+
 def pin_assign_brute_force(lib):
     """On small random inputs the result equals the definition: parent = first
     arg min of the exact squared distance over the parents; final = first arg
@@ -178,11 +198,9 @@ def pin_importance_closed_form(lib):
     counts = np.array([[3, 5, 0, 0, 0, 0]], np.int32)
     a, b = 0.7, -0.4
     Q = np.array([[[2 * a, 2 * b]]])  # with scale 0.5 the logits are a and b
-    w = _O(lib, 1, 1, 1, d, M0, C).importance_f64(Q, cb, counts, 1, 0.5)
+    w = _O(lib, 1, 1, 1, d, M0, C).importance(Q, cb, counts, 1, 0.5)
     w1 = np.exp(a) * 3 / (np.exp(a) * 3 + np.exp(b) * 5)
     np.testing.assert_allclose(w[0, 0], [w1, 1 - w1, 0.0], rtol=1e-12, atol=1e-15)
-    wf = _O(lib, 1, 1, 1, d, M0, C).importance(Q, cb, counts, 1, 0.5)
-    np.testing.assert_allclose(wf[0, 0], [w1, 1 - w1, 0.0], rtol=1e-6, atol=1e-7)
 
 
 def pin_importance_properties(lib):
@@ -196,15 +214,14 @@ def pin_importance_properties(lib):
     _, counts = o.aggregate(data["V"], parent, row)
     counts = counts.copy()
     counts[0, 3] = 0  # an empty parent
-    for w in (o.importance(data["Q"], data["codebook"], counts, 64, cfg.scale),
-              o.importance_f64(data["Q"], data["codebook"], counts, 64, cfg.scale)):
-        assert (w >= 0).all()
-        assert (w[0, :, 3] == 0).all() and (w[0, :, [0, 1, 2, 4]] > 0).all()
-        sizes = np.array([64] * 15 + [1000 - 15 * 64], np.float64)
-        np.testing.assert_allclose(w.sum(-1)[0], sizes, rtol=1e-5 if w.dtype == np.float32 else 1e-12)
+    w = o.importance(data["Q"], data["codebook"], counts, 64, cfg.scale)
+    assert (w >= 0).all()
+    assert (w[0, :, 3] == 0).all() and (w[0, :, [0, 1, 2, 4]] > 0).all()
+    sizes = np.array([64] * 15 + [1000 - 15 * 64], np.float64)
+    np.testing.assert_allclose(w.sum(-1)[0], sizes, rtol=1e-12)
     Q = np.repeat(data["codebook"][0, 7][None, None, :] * 6.0, 64, axis=1)
     o1 = _O(lib, 1, 1, 64, cfg.d, cfg.M0, cfg.C)
-    w = o1.importance_f64(Q, data["codebook"], counts, 64, cfg.scale)
+    w = o1.importance(Q, data["codebook"], counts, 64, cfg.scale)
     assert int(np.argmax(w[0, 0])) == 7
 
 
@@ -212,13 +229,15 @@ def pin_select(lib):
     """Alg. 2, the parent choice: the P largest importances, ties to the lower index,
     written ascending; P = M0 selects every parent, P = 0 none."""
     o = _O(lib, 1, 1, 1, 1, 6, 1)
-    w = np.array([[0.5, 2.0, 2.0, 0.1, 3.0, 0.5]], np.float32)
+    w = np.array([[0.5, 2.0, 2.0, 0.1, 3.0, 0.5]])
     assert o.select(w, 3).tolist() == [[1, 2, 4]]
     assert o.select(w, 4).tolist() == [[0, 1, 2, 4]]
     assert o.select(w, 6).tolist() == [[0, 1, 2, 3, 4, 5]]
     assert o.select(w, 0).shape == (1, 0)
+    # importances closer than single precision resolves are still ordered
+    assert o.select(np.array([[1.0, 1.0 + 2.0 ** -30, 0.5, 0.0, 0.0, 0.0]]), 1).tolist() == [[1]]
     rng = np.random.default_rng(5)
-    W = rng.integers(0, 4, size=(50, 6)).astype(np.float32)
+    W = rng.integers(0, 4, size=(50, 6)).astype(np.float64)
     for P in range(7):
         sel = o.select(W, P)
         for r in range(50):
@@ -450,7 +469,7 @@ def pin_importance_tiled(lib):
     _, counts = o.aggregate(data["V"], parent, row)
     bq, scale, M0 = cfg.block_q, cfg.scale, cfg.M0
     Q, cb = data["Q"], data["codebook"]
-    exact = o.importance_f64(Q, cb, counts, bq, scale)
+    exact = o.importance(Q, cb, counts, bq, scale)
     nq = np.array([min(cfg.N, (t + 1) * bq) - t * bq for t in range(o.tiles(bq))], np.float64)
     n = counts[:, :M0].astype(np.float64)
     ntot = n.sum(axis=1)
@@ -470,15 +489,14 @@ def pin_importance_tiled(lib):
 
 # ---------------------------------------------------------------- query order
 def _run_ordered(o, data, counts, vsum, order, P, bq, scale):
-    """Importance (float and double), selection and output with the query tiles
-    taken along ``order``, through the oracle's ordering step."""
+    """Importance, selection and output with the query tiles taken along
+    ``order``, through the oracle's ordering step."""
     oq, Qo, rows = o.ordered(data["Q"], order)
     cb = data["codebook"]
     w = oq.importance(Qo, cb, counts, bq, scale)
-    w64 = oq.importance_f64(Qo, cb, counts, bq, scale)
     sel = oq.select(w, P)
     Y = o.scatter_rows(oq.attention_substituted(Qo, cb, vsum, counts, sel, P, bq, scale), rows)
-    return w64, sel, Y
+    return w, sel, Y
 
 
 def _ordered_setup(lib, seed, N=96, M0=6, C=3):
@@ -507,7 +525,7 @@ def pin_order_tile_relabel(lib):
         elif t == 4:
             r = np.roll(r, 5)
         order[t * bq:(t + 1) * bq] = r
-    w_ref = o.importance_f64(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    w_ref = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
     sel_ref = o.select(o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale), P)
     Y_ref = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel_ref, P, bq, cfg.scale)
     w, sel, Y = _run_ordered(o, data, counts, vsum, order, P, bq, cfg.scale)
@@ -725,6 +743,7 @@ PINS = {
     "counts_and_sums": pin_counts_and_sums,
     "key_order": pin_key_order,
     "aggregate_segments": pin_aggregate_segments,
+    "assign_exact_arithmetic": pin_assign_exact_arithmetic,
     "importance_closed_form": pin_importance_closed_form,
     "importance_properties": pin_importance_properties,
     "select": pin_select,

@@ -41,13 +41,13 @@ def test_tiled_selection_capture():
         onehot[np.arange(cfg.N), parent[bh]] = 1.0
         per_parent = A @ onehot                      # [N queries, M0]
         mass[bh] = per_parent.reshape(T, bq, cfg.M0).mean(axis=1)
-    w = o.importance_f64(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    w = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
     wt = o.importance_tiled_f64(data["Q"], data["codebook"], counts, bq, cfg.scale, 64)
     for P in (4, 8, 16, 32):
         caps = {
-            "exact": _capture(mass, o.select(mass.astype(np.float32), P)),
-            "non-tiled": _capture(mass, o.select(w.astype(np.float32), P)),
-            "tiled (64)": _capture(mass, o.select(wt.astype(np.float32), P)),
+            "exact": _capture(mass, o.select(mass, P)),
+            "non-tiled": _capture(mass, o.select(w, P)),
+            "tiled (64)": _capture(mass, o.select(wt, P)),
         }
         print(f"[capture] M0 {cfg.M0} P {P:2d}: " +
               "  ".join(f"{k} {v.mean() * 100:6.2f}%" for k, v in caps.items()))

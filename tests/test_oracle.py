@@ -34,8 +34,10 @@ MUTANTS = [
     ("empty children not masked", "double dA = n[c0 + c] > 0 ? exp(s[c] - m) - exp(sp - m) : 0.0;",
      "double dA = exp(s[c] - m) - exp(sp - m);"),
     ("running max over empty children", "if (n[c0 + c] > 0 && s[c] > mnew) mnew = s[c];", "if (s[c] > mnew) mnew = s[c];"),
-    ("importance without counts", "wt[j] += expf(s[j] - m) * (float)n[j] / Z;", "wt[j] += expf(s[j] - m) / Z;"),
-    ("importance without the logit scale", "s[j] = (float)scale * acc;", "s[j] = acc;"),
+    ("importance without counts", "if (n[j] > 0) w[j] += exp(s[j] - m) * n[j] / Z;",
+     "if (n[j] > 0) w[j] += exp(s[j] - m) / Z;"),
+    ("importance without the logit scale", "s[j] = scale * dotd(q, cbh + (int64_t)j * d, d);\n            if (n[j] > 0 && s[j] > m) m = s[j];\n        }\n        double Z",
+     "s[j] = dotd(q, cbh + (int64_t)j * d, d);\n            if (n[j] > 0 && s[j] > m) m = s[j];\n        }\n        double Z"),
     ("top-P ties to the higher index", "if (wr[jj] > wr[j] || (wr[jj] == wr[j] && jj < j)) ++ahead;",
      "if (wr[jj] > wr[j] || (wr[jj] == wr[j] && jj > j)) ++ahead;"),
     ("parent rows miss the moved keys", "ct[a] += 1;", "ct[a] += (r == a);"),
@@ -55,6 +57,11 @@ MUTANTS = [
      "Sh[x * d + t] = (1.0 - decay) * Sh[x * d + t] + decay * kb[t];"),
     ("unweighted projection", "if (zeros == 0) share = 1.0 / (n * sigma);", "if (zeros == 0) share = 1.0 / C;"),
     ("massless children keep their place", "else share = n > 0.0 ? 0.0 : 1.0 / zeros;", "else share = 0.0;"),
+    ("parent choice in single precision", "if (dm < dbest) { dbest = dm; a = m; }",
+     "if ((float)dm < (float)dbest) { dbest = dm; a = m; }"),
+    ("move decision in single precision", "(C > 0 && dchild < dbest)", "(C > 0 && (float)dchild < (float)dbest)"),
+    ("selection in single precision", "if (wr[jj] > wr[j] || (wr[jj] == wr[j] && jj < j)) ++ahead;",
+     "if ((float)wr[jj] > (float)wr[j] || ((float)wr[jj] == (float)wr[j] && jj < j)) ++ahead;"),
     ("count EMA uses the old count twice", "Nh[x] = decay * Nh[x] + (1.0 - decay) * cnt;", "Nh[x] = decay * Nh[x] + (1.0 - decay) * Nh[x];"),
 ]
 

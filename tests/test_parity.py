@@ -39,7 +39,7 @@ def _full_check(data, P, bq=None):
     vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
     check_vsum(g["vsum"], vsum, vabs, counts)
     w = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
-    w64 = o.importance_f64(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    w64 = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
     werr = np.abs(g["importance"].astype(np.float64) - w64).max()
     say(f"  importance max|err| = {werr:.3e}")
     assert werr <= 1e-5 * bq
@@ -147,7 +147,7 @@ def test_approx_denominator(d, M0, P):
     srt = -np.sort(-w64, axis=-1)
     margin = (srt[..., P - 1] - srt[..., P]) / np.maximum(srt[..., P - 1], 1.0)
     decisive = (margin >= 1e-4) | ((srt[..., P - 1] == 0.0) & (srt[..., P] == 0.0))
-    sel = o.select(w64.astype(np.float32), P)
+    sel = o.select(w64, P)
     say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
     assert decisive.mean() > 0.8
     assert np.array_equal(g["sel"][decisive], sel[decisive])
@@ -195,7 +195,7 @@ def _ordered_check(data, P, order, approx=False, nan_fill=False):
         w = w64.astype(np.float32)
     else:
         w = oq.importance(Qo, cb, counts, bq, cfg.scale)
-        w64 = oq.importance_f64(Qo, cb, counts, bq, cfg.scale)
+        w64 = oq.importance(Qo, cb, counts, bq, cfg.scale)
     T = w64.shape[1]
     werr = np.abs(g["importance"][:, :T].astype(np.float64) - w64).max()
     say(f"  importance max|err| = {werr:.3e}")
@@ -340,7 +340,7 @@ def _decisive_check(data, P, scale, where):
     vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
     check_vsum(g["vsum"], vsum, vabs, counts)
     w = o.importance(data["Q"], data["codebook"], counts, bq, scale)
-    w64 = o.importance_f64(data["Q"], data["codebook"], counts, bq, scale)
+    w64 = o.importance(data["Q"], data["codebook"], counts, bq, scale)
     werr = np.abs(g["importance"].astype(np.float64) - w64).max()
     say(f"  importance max|err| = {werr:.3e}")
     assert werr <= 1e-5 * bq
