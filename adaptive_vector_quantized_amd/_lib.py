@@ -87,10 +87,78 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+# The C interface sees only pointers and sizes, so the binding is where every
+# tensor is checked against the sizes it will be read or written with: dtype,
+# shape and layout of every tensor first, then (_on_device) that all of them
+# are device memory on the device of the call's first tensor.
+def _check(t, name: str, shape, dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _on_device(named):
+    """named: (name, tensor or None) pairs; the first tensor's device is the call's."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {dev}")
+
+
 def _shape4(t: torch.Tensor, name: str) -> Tuple[int, int, int, int]:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    _dtype_code(t)
     if t.dim() != 4 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
     return tuple(t.shape)
+
+
+def _codebook_rows(codebook, H: int, d: int, dtype, C: int) -> Tuple[int, int]:
+    """(Mt, M0) of a [H, M0 * (1 + C), d] codebook in the activations' dtype."""
+    if not isinstance(C, int) or C < 0:
+        raise ValueError(f"C must be a non-negative int, got {C!r}")
+    if not isinstance(codebook, torch.Tensor) or codebook.dim() != 3:
+        raise ValueError("codebook must be an [H, M0 * (1 + C), d] tensor")
+    Mt = int(codebook.shape[1])
+    _check(codebook, "codebook", (H, Mt, d), dtype)
+    if Mt == 0 or Mt % (1 + C):
+        raise ValueError(f"codebook rows ({Mt}) must be M0 * (1 + C) with M0 >= 1, C = {C}")
+    return Mt, Mt // (1 + C)
+
+
+def _assign_args(K, V, codebook, C, vsum, counts, assign, ksum, want_assign, with_keys):
+    B, H, N, d = _shape4(K, "K")
+    dev = K.device
+    _check(V, "V", (B, H, N, d), K.dtype)
+    Mt, M0 = _codebook_rows(codebook, H, d, K.dtype, C)
+    for name, t, shape in (("vsum", vsum, (B, H, Mt, d)), ("counts", counts, (B, H, Mt)),
+                           ("assign", assign, (B, H, N)), ("ksum", ksum if with_keys else None, (B, H, Mt, d))):
+        if t is not None:
+            _check(t, name, shape, torch.int32 if name in ("counts", "assign") else torch.float32)
+    _on_device([("K", K), ("V", V), ("codebook", codebook), ("vsum", vsum), ("counts", counts),
+                ("assign", assign), ("ksum", ksum if with_keys else None)])
+    if vsum is None:
+        vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
+    if want_assign and assign is None:
+        assign = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    if with_keys and ksum is None:
+        ksum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
+    return (B, H, N, d, M0), vsum, counts, assign, ksum
 
 
 def assign_aggregate(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C: int, *,
@@ -98,22 +166,8 @@ def assign_aggregate(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C
                      counts: Optional[torch.Tensor] = None, assign: Optional[torch.Tensor] = None):
     """Kernel 1.  K, V: [B, H, N, d]; codebook: [H, M0*(1+C), d] (same dtype).
     Returns (vsum [B, H, Mt, d] float32, counts [B, H, Mt] int32, assign [B, H, N] int32 or None)."""
-    B, H, N, d = _shape4(K, "K")
-    if tuple(V.shape) != (B, H, N, d) or V.dtype != K.dtype or not V.is_contiguous():
-        raise ValueError("V must match K")
-    if codebook.dim() != 3 or codebook.shape[0] != H or codebook.shape[2] != d or not codebook.is_contiguous():
-        raise ValueError("codebook must be a contiguous [H, Mt, d] tensor")
-    Mt = codebook.shape[1]
-    if Mt % (1 + C):
-        raise ValueError("codebook rows must be M0 * (1 + C)")
-    M0 = Mt // (1 + C)
-    dev = K.device
-    if vsum is None:
-        vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
-    if counts is None:
-        counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
-    if want_assign and assign is None:
-        assign = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    (B, H, N, d, M0), vsum, counts, assign, _ = _assign_args(K, V, codebook, C, vsum, counts, assign, None,
+                                                            want_assign, False)
     rc = _lib.avq_assign_aggregate(_ptr(K), _ptr(V), _ptr(codebook), B, H, N, d, M0, C, _dtype_code(K),
                                    _ptr(vsum), _ptr(counts), _ptr(assign), _stream(K))
     if rc != 0:
@@ -127,24 +181,8 @@ def assign_aggregate_kv(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor
                         ksum: Optional[torch.Tensor] = None):
     """Kernel 1 with the keys also summed per codeword (for codebook_update), in one pass.
     Returns (vsum, counts, assign or None, ksum [B, H, Mt, d] float32)."""
-    B, H, N, d = _shape4(K, "K")
-    if tuple(V.shape) != (B, H, N, d) or V.dtype != K.dtype or not V.is_contiguous():
-        raise ValueError("V must match K")
-    if codebook.dim() != 3 or codebook.shape[0] != H or codebook.shape[2] != d or not codebook.is_contiguous():
-        raise ValueError("codebook must be a contiguous [H, Mt, d] tensor")
-    Mt = codebook.shape[1]
-    if Mt % (1 + C):
-        raise ValueError("codebook rows must be M0 * (1 + C)")
-    M0 = Mt // (1 + C)
-    dev = K.device
-    if vsum is None:
-        vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
-    if counts is None:
-        counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
-    if ksum is None:
-        ksum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
-    if want_assign and assign is None:
-        assign = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    (B, H, N, d, M0), vsum, counts, assign, ksum = _assign_args(K, V, codebook, C, vsum, counts, assign, ksum,
+                                                               want_assign, True)
     rc = _lib.avq_assign_aggregate_kv(_ptr(K), _ptr(V), _ptr(codebook), B, H, N, d, M0, C, _dtype_code(K),
                                       _ptr(vsum), _ptr(counts), _ptr(assign), _ptr(ksum), _stream(K))
     if rc != 0:
@@ -169,12 +207,21 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
     ``gilbert.query_order``) selects avq_attention_fwd_ordered: tile t holds the
     queries of rows query_order[t*block_q ...]; Y stays in the row order of Q."""
     B, H, N, d = _shape4(Q, "Q")
-    Mt = codebook.shape[1]
-    M0 = Mt // (1 + C)
+    dev = Q.device
+    Mt, M0 = _codebook_rows(codebook, H, d, Q.dtype, C)
+    _check(vsum, "vsum", (B, H, Mt, d), torch.float32)
+    _check(counts, "counts", (B, H, Mt), torch.int32)
+    if Y is not None:
+        _check(Y, "Y", (B, H, N, d), torch.float32)
+    if workspace is not None:
+        _check(workspace, "workspace", None, torch.uint8)
+    if query_order is not None:
+        _check(query_order, "query_order", (N,), torch.int32)
+    _on_device([("Q", Q), ("codebook", codebook), ("vsum", vsum), ("counts", counts), ("Y", Y),
+                ("workspace", workspace), ("query_order", query_order)])
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
-    dev = Q.device
-    T = (N + block_q - 1) // block_q
+    T = (N + block_q - 1) // block_q if block_q > 0 else 0
     if Y is None:
         Y = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     topp = torch.empty((B, H, T, P), dtype=torch.int32, device=dev) if want_topp else None
@@ -182,14 +229,8 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
     need = workspace_size(B, H, d, M0, C, Q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    for name, t in (("vsum", vsum), ("counts", counts)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = workspace.numel()
     if query_order is not None:
-        if (query_order.dtype != torch.int32 or query_order.dim() != 1 or query_order.numel() != N
-                or not query_order.is_contiguous() or query_order.device != dev):
-            raise ValueError("query_order must be a contiguous int32 [N] tensor on the device of Q")
         name = "avq_attention_fwd_ordered"
         rc = _lib.avq_attention_fwd_ordered(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
                                             _dtype_code(Q), P, block_q, float(scale), _ptr(query_order),
@@ -218,17 +259,19 @@ def codebook_update(ksum: torch.Tensor, counts: torch.Tensor, S: torch.Tensor, N
     """Codebook update step (App. A, Eq. 11-12), in place on S [H, Mt, d], Nema [H, Mt] and
     codebook [H, Mt, d] (all float32).  ksum [B, H, Mt, d] float32 and counts [B, H, Mt] int32 are
     this batch's per-codeword key sums and counts: assign_aggregate(K, K, ...)."""
-    if ksum.dim() != 4 or ksum.dtype != torch.float32 or not ksum.is_contiguous():
-        raise ValueError("ksum must be a contiguous float32 [B, H, Mt, d] tensor")
-    B, H, Mt, d = ksum.shape
-    if Mt % (1 + C):
+    if not isinstance(ksum, torch.Tensor) or ksum.dim() != 4:
+        raise ValueError("ksum must be a float32 [B, H, Mt, d] tensor")
+    B, H, Mt, d = (int(x) for x in ksum.shape)
+    _check(ksum, "ksum", (B, H, Mt, d), torch.float32)
+    if not isinstance(C, int) or C < 0:
+        raise ValueError(f"C must be a non-negative int, got {C!r}")
+    if Mt == 0 or Mt % (1 + C):
         raise ValueError("codeword rows must be M0 * (1 + C)")
     M0 = Mt // (1 + C)
-    if tuple(counts.shape) != (B, H, Mt) or counts.dtype != torch.int32 or not counts.is_contiguous():
-        raise ValueError("counts must be a contiguous int32 [B, H, Mt] tensor")
+    _check(counts, "counts", (B, H, Mt), torch.int32)
     for name, t, shape in (("S", S, (H, Mt, d)), ("Nema", Nema, (H, Mt)), ("codebook", codebook, (H, Mt, d))):
-        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor")
+        _check(t, name, shape, torch.float32)
+    _on_device([("ksum", ksum), ("counts", counts), ("S", S), ("Nema", Nema), ("codebook", codebook)])
     rc = _lib.avq_codebook_update(_ptr(ksum), _ptr(counts), B, H, d, M0, C, float(decay), _ptr(S), _ptr(Nema),
                                   _ptr(codebook), _stream(S))
     if rc != 0:

@@ -88,6 +88,36 @@ def compare_y(g_Y, o_Y, dtype: str, where=""):
     return err / scale
 
 
+def check_topp(g_sel, g_imp, w_ref, P: int, where=""):
+    """Top-P sets on tiles whose reference decision is not drawn clear of ties,
+    where several sets can be right: (1) the GPU's set is exactly the top-P of
+    the GPU's own importances (larger first, equal ones to the lower index),
+    and (2) against the double-precision reference importances every chosen
+    parent is at least as important as every unchosen one, up to twice the
+    largest importance error (if the GPU ranks by its own importances, a pair
+    can only swap within that).  Returns the fraction of tiles whose set equals
+    the reference's own top-P."""
+    R = int(np.prod(w_ref.shape[:-1]))
+    M0 = w_ref.shape[-1]
+    g_sel = np.asarray(g_sel).reshape(R, P)
+    g_imp = np.asarray(g_imp, np.float64).reshape(R, M0)
+    w_ref = np.asarray(w_ref, np.float64).reshape(R, M0)
+    own = np.sort(np.argsort(-g_imp, axis=-1, kind="stable")[:, :P], axis=-1)
+    bad = np.argwhere((own != g_sel).any(-1))
+    assert bad.size == 0, f"{where}: GPU set is not the top-P of its own importances at rows {bad[:5].ravel()}"
+    chosen = np.zeros((R, M0), bool)
+    np.put_along_axis(chosen, g_sel.astype(np.int64), True, axis=-1)
+    tol = 2.0 * np.abs(g_imp - w_ref).max() + 1e-12
+    lo = np.where(chosen, w_ref, np.inf).min(-1)
+    hi = np.where(chosen, -np.inf, w_ref).max(-1)
+    viol = np.argwhere(lo < hi - tol)
+    assert viol.size == 0, f"{where}: chosen importance below an unchosen one at rows {viol[:5].ravel()}"
+    ref = np.sort(np.argsort(-w_ref, axis=-1, kind="stable")[:, :P], axis=-1)
+    same = float((ref == g_sel).all(-1).mean())
+    say(f"  top-P valid on every tile (tol {tol:.2e}); equal to the reference set on {same * 100:.1f}%")
+    return same
+
+
 def sub_problem(data: dict, bh: int, t: int):
     """Queries of one tile of one (batch, head) as a stand-alone problem for the
     oracle's per-tile steps (importance, selection, output)."""

@@ -169,3 +169,98 @@ def test_codebook_update_validation(L):
     assert upd(ksum=None) == -1
     assert upd(counts=ctypes.c_void_p(p.value + 2)) == -4
     assert upd(H=0, S=None) == 0      # no head: nothing to do
+
+
+# ---- the Python binding's checks (CPU tensors: every structural mismatch is
+# reported before the device check, and a tensor that is not GPU memory is
+# refused; nothing reaches the C interface) --------------------------------
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _assign_inputs(dtype=None):
+    import torch
+    dt = dtype or torch.bfloat16
+    B, H, N, d, M0, C = 1, 2, 40, 64, 4, 2
+    Mt = M0 * (1 + C)
+    return dict(K=_t((B, H, N, d), dt), V=_t((B, H, N, d), dt), codebook=_t((H, Mt, d), dt), C=C), (B, H, N, d, Mt)
+
+
+@pytest.mark.parametrize("kv", [False, True])
+def test_binding_assign_checks(kv):
+    import torch
+    from adaptive_vector_quantized_amd import _lib
+    fn = _lib.assign_aggregate_kv if kv else _lib.assign_aggregate
+    a, (B, H, N, d, Mt) = _assign_inputs()
+    cases = [
+        (dict(V=_t((B, H, N, d), torch.float32)), TypeError, "V must be torch.bfloat16"),
+        (dict(V=_t((B, H, N + 1, d), torch.bfloat16)), ValueError, "V must have shape"),
+        (dict(codebook=_t((H, Mt, d), torch.float32)), TypeError, "codebook must be torch.bfloat16"),
+        (dict(codebook=_t((H + 1, Mt, d), torch.bfloat16)), ValueError, "codebook must have shape"),
+        (dict(codebook=_t((H, Mt + 1, d), torch.bfloat16)), ValueError, "must be M0 * (1 + C)"),
+        (dict(C=-1), ValueError, "C must be"),
+        (dict(K=_t((B, H, N, d), torch.float16)), TypeError, "unsupported dtype"),
+        (dict(K=_t((B, H, d, N), torch.bfloat16).transpose(2, 3)), ValueError, "contiguous"),
+        (dict(vsum=_t((B, H, Mt, d), torch.bfloat16)), TypeError, "vsum must be torch.float32"),
+        (dict(vsum=_t((B, H, Mt - 1, d), torch.float32)), ValueError, "vsum must have shape"),
+        (dict(counts=_t((B, H, Mt), torch.int64)), TypeError, "counts must be torch.int32"),
+        (dict(counts=_t((B, H, Mt + 3), torch.int32)), ValueError, "counts must have shape"),
+        (dict(assign=_t((B, H, N - 1), torch.int32)), ValueError, "assign must have shape"),
+        ({}, ValueError, "must be a GPU tensor"),
+    ]
+    if kv:
+        cases.append((dict(ksum=_t((B, H, Mt, d + 1), torch.float32)), ValueError, "ksum must have shape"))
+    for over, exc, msg in cases:
+        kw = dict(a, **over)
+        with pytest.raises(exc, match=re.escape(msg)):
+            fn(kw.pop("K"), kw.pop("V"), kw.pop("codebook"), kw.pop("C"), **kw)
+
+
+def test_binding_attention_checks():
+    import torch
+    from adaptive_vector_quantized_amd import _lib
+    B, H, N, d, M0, C = 1, 2, 40, 64, 4, 2
+    Mt = M0 * (1 + C)
+    base = dict(Q=_t((B, H, N, d), torch.bfloat16), codebook=_t((H, Mt, d), torch.bfloat16),
+                vsum=_t((B, H, Mt, d), torch.float32), counts=_t((B, H, Mt), torch.int32))
+    cases = [
+        (dict(codebook=_t((H, Mt, d), torch.float32)), TypeError, "codebook must be torch.bfloat16"),
+        (dict(codebook=_t((H, Mt, d + 64), torch.bfloat16)), ValueError, "codebook must have shape"),
+        (dict(codebook=_t((H, Mt + 2, d), torch.bfloat16)), ValueError, "must be M0 * (1 + C)"),
+        (dict(vsum=_t((B, H, Mt, d), torch.bfloat16)), TypeError, "vsum must be torch.float32"),
+        (dict(vsum=_t((B, H + 1, Mt, d), torch.float32)), ValueError, "vsum must have shape"),
+        (dict(counts=_t((B, H, Mt), torch.float32)), TypeError, "counts must be torch.int32"),
+        (dict(counts=_t((B, H, Mt, 1), torch.int32)), ValueError, "counts must have shape"),
+        (dict(Y=_t((B, H, N, d), torch.bfloat16)), TypeError, "Y must be torch.float32"),
+        (dict(Y=_t((B, H, N - 1, d), torch.float32)), ValueError, "Y must have shape"),
+        (dict(workspace=_t((64,), torch.float32)), TypeError, "workspace must be torch.uint8"),
+        (dict(query_order=_t((N,), torch.int64)), TypeError, "query_order must be torch.int32"),
+        (dict(query_order=_t((N + 1,), torch.int32)), ValueError, "query_order must have shape"),
+        ({}, ValueError, "must be a GPU tensor"),
+    ]
+    for over, exc, msg in cases:
+        kw = dict(base, **over)
+        with pytest.raises(exc, match=re.escape(msg)):
+            _lib.attention_fwd(kw.pop("Q"), kw.pop("codebook"), kw.pop("vsum"), kw.pop("counts"), C, 2, 64, **kw)
+
+
+def test_binding_update_checks():
+    import torch
+    from adaptive_vector_quantized_amd import _lib
+    B, H, d, M0, C = 2, 2, 64, 4, 2
+    Mt = M0 * (1 + C)
+    base = dict(ksum=_t((B, H, Mt, d), torch.float32), counts=_t((B, H, Mt), torch.int32),
+                S=_t((H, Mt, d), torch.float32), Nema=_t((H, Mt), torch.float32), codebook=_t((H, Mt, d), torch.float32))
+    cases = [
+        (dict(ksum=_t((B, H, Mt, d), torch.bfloat16)), TypeError, "ksum must be torch.float32"),
+        (dict(counts=_t((B, H, Mt - 1), torch.int32)), ValueError, "counts must have shape"),
+        (dict(S=_t((H, Mt, d), torch.bfloat16)), TypeError, "S must be torch.float32"),
+        (dict(Nema=_t((H, Mt + 1), torch.float32)), ValueError, "Nema must have shape"),
+        (dict(codebook=_t((H, Mt, d), torch.bfloat16)), TypeError, "codebook must be torch.float32"),
+        ({}, ValueError, "must be a GPU tensor"),
+    ]
+    for over, exc, msg in cases:
+        kw = dict(base, **over)
+        with pytest.raises(exc, match=re.escape(msg)):
+            _lib.codebook_update(kw["ksum"], kw["counts"], kw["S"], kw["Nema"], kw["codebook"], C, 0.9)

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from adaptive_vector_quantized_amd import gen, gilbert
-from parity_util import check_vsum, compare_y, run_attention_variants, run_gpu, say, sub_problem
+from parity_util import check_topp, check_vsum, compare_y, run_attention_variants, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -39,8 +39,7 @@ def _full_check(data, P, bq=None):
     vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
     check_vsum(g["vsum"], vsum, vabs, counts)
     w = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
-    w64 = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
-    werr = np.abs(g["importance"].astype(np.float64) - w64).max()
+    werr = np.abs(g["importance"].astype(np.float64) - w).max()
     say(f"  importance max|err| = {werr:.3e}")
     assert werr <= 1e-5 * bq
     if P > 0:
@@ -50,6 +49,7 @@ def _full_check(data, P, bq=None):
         sel = np.zeros((cfg.BH, (cfg.N + bq - 1) // bq, 0), np.int32)
     Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel, P, bq, cfg.scale)
     compare_y(g["Y"], Y, cfg.dtype, f"{cfg.name} P={P}")
+    return g, Y
 
 
 @pytest.mark.parametrize("seed", [1000, 1, 2, 3])
@@ -151,6 +151,7 @@ def test_approx_denominator(d, M0, P):
     say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
     assert decisive.mean() > 0.8
     assert np.array_equal(g["sel"][decisive], sel[decisive])
+    check_topp(g["sel"], g["importance"], w64, P, f"approx d{d} M0{M0}")
     Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, g["sel"], P, bq, cfg.scale)
     compare_y(g["Y"], Y, cfg.dtype, f"approx d{d} M0{M0} P{P}")
     if M0 <= 64:
@@ -192,9 +193,7 @@ def _ordered_check(data, P, order, approx=False, nan_fill=False):
     cb = data["codebook"]
     if approx:
         w64 = oq.importance_tiled_f64(Qo, cb, counts, bq, cfg.scale, 64)
-        w = w64.astype(np.float32)
     else:
-        w = oq.importance(Qo, cb, counts, bq, cfg.scale)
         w64 = oq.importance(Qo, cb, counts, bq, cfg.scale)
     T = w64.shape[1]
     werr = np.abs(g["importance"][:, :T].astype(np.float64) - w64).max()
@@ -204,10 +203,11 @@ def _ordered_check(data, P, order, approx=False, nan_fill=False):
         srt = -np.sort(-w64, axis=-1)
         margin = (srt[..., P - 1] - srt[..., P]) / np.maximum(srt[..., P - 1], 1.0)
         decisive = (margin >= 1e-4) | ((srt[..., P - 1] == 0.0) & (srt[..., P] == 0.0))
-        sel = oq.select(w, P)
+        sel = oq.select(w64, P)
         say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
         assert decisive.mean() > 0.9
         assert np.array_equal(g["sel"][:, :T][decisive], sel[decisive])
+        check_topp(g["sel"][:, :T], g["importance"][:, :T], w64, P, f"ordered {cfg.name}")
         sel = g["sel"][:, :T]
     else:
         sel = np.zeros((cfg.BH, T, 0), np.int32)
@@ -259,67 +259,76 @@ def test_ordered_flat_codebook():
 
 @pytest.mark.parametrize("M0", [64, 256, 512])
 def test_flat_codebook(M0):
-    """C = 0: a flat codebook of M0 codewords, plain VQ attention (P = 0)."""
-    _full_check(_data("grid64", M0=M0, C=0, P=0), 0)
+    """C = 0: a flat codebook of M0 codewords, plain VQ attention (P = 0); also
+    in the launch the benchmark times (no importance output: no importance
+    partials in LDS and no importance barrier)."""
+    data = _data("grid64", M0=M0, C=0, P=0)
+    _, Y = _full_check(data, 0)
+    g = run_gpu(data, 0, want_topp=False, want_importance=False)
+    compare_y(g["Y"], Y, data["cfg"].dtype, f"flat M0={M0}, no importance output")
 
 
-def test_full_size_grid128():
-    """The headline workload at full size: every assignment, count and value
-    sum, plus sampled query tiles for importance, top-P and output."""
-    data = _data("grid128")
+def _full_size(name, P=None):
+    """A workload at its full size, in the launch configuration the benchmark
+    times, compared everywhere: every assignment, count and value sum, every
+    tile's importances and top-P set, every output element."""
+    data = _data(name)
     cfg = data["cfg"]
-    say(f"[parity] grid128 full size B{cfg.B} H{cfg.H} N{cfg.N}")
-    g = run_gpu(data, cfg.P)
+    P = cfg.P if P is None else P
+    _full_check(data, P)
+
+
+@pytest.mark.timeout(600)
+def test_full_size_grid128():
+    """The headline workload (B2 H16 N16384 d64 M0 64 C8 P16, 128-query tiles)
+    at full size: all 4096 tiles."""
+    _full_size("grid128")
+
+
+@pytest.mark.timeout(900)
+def test_full_size_grid256():
+    """The 256x256-grid workload (B1 H8 N65536 d128 M0 256 C8 P32, exact
+    two-pass denominator, several query tiles per workgroup) at full size: all
+    4096 tiles."""
+    _full_size("grid256")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("P", [0, 4, 16, 64])
+def test_sweep(P):
+    """The refinement-budget sweep (B1 H16 N16384 d64 M0 64 C8) at each P, in
+    the launch the benchmark times: no importance or top-P output.  The output
+    is compared with the substituted-codebook form for the oracle's selection
+    (the sweep's inputs are drawn clear of top-P ties at every P of the sweep;
+    P = 64 = M0 refines every parent); one more launch with the importance
+    output checks that it selects the same sets."""
+    data = _data("sweep")
+    cfg = data["cfg"]
+    bq = cfg.block_q
+    say(f"[parity] sweep P={P} B{cfg.B} H{cfg.H} N{cfg.N}, launch without importance/top-P outputs")
+    g = run_gpu(data, P, want_topp=False, want_importance=False)
     o = oracle.Oracle.for_cfg(cfg)
     parent, row = o.assign(data["K"], data["codebook"])
     assert np.array_equal(g["row"], row)
     vsum, counts = o.aggregate(data["V"], parent, row)
     assert np.array_equal(g["counts"], counts)
-    vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
-    check_vsum(g["vsum"], vsum, vabs, counts)
-    rng = np.random.default_rng(7)
-    picks = [(int(rng.integers(cfg.BH)), int(rng.integers(cfg.tiles))) for _ in range(48)] + [(cfg.BH - 1, cfg.tiles - 1)]
-    for bh, t in picks:
-        h = bh % cfg.H
-        Qt, i0, i1 = sub_problem(data, bh, t)
-        os_ = oracle.Oracle(1, 1, i1 - i0, cfg.d, cfg.M0, cfg.C)
-        cbh = data["codebook"][h:h + 1]
-        w = os_.importance(Qt, cbh, counts[bh:bh + 1], cfg.block_q, cfg.scale)
-        sel = os_.select(w, cfg.P)
-        assert np.array_equal(g["sel"][bh, t], sel[0, 0]), (bh, t)
-        Y = os_.attention_substituted(Qt, cbh, vsum[bh:bh + 1], counts[bh:bh + 1], sel, cfg.P, cfg.block_q, cfg.scale)
-        compare_y(g["Y"][bh:bh + 1, i0:i1], Y, cfg.dtype, f"grid128 bh{bh} tile{t}")
+    w = o.importance(data["Q"], data["codebook"], counts, bq, cfg.scale)
+    sel = o.select(w, P)
+    if 0 < P < cfg.M0:
+        g2 = run_gpu(data, P)
+        assert np.array_equal(g2["sel"], sel)
+    Y = o.attention_substituted(data["Q"], data["codebook"], vsum, counts, sel, P, bq, cfg.scale)
+    compare_y(g["Y"], Y, cfg.dtype, f"sweep P={P}")
 
 
+@pytest.mark.timeout(600)
 def test_full_size_grid128_gilbert():
     """The headline workload at full size with its queries along the Gilbert
     curve of the 128x128 grid, in the launch configuration the benchmark times
-    with --query-order gilbert: sampled tiles checked one by one."""
+    with --query-order gilbert: all tiles."""
     data = _data("grid128")
-    cfg = data["cfg"]
     order = gilbert.query_order(128, 128)
-    d2 = _place_along(data, order)
-    say(f"[parity] grid128 full size, Gilbert order B{cfg.B} H{cfg.H} N{cfg.N}")
-    g = run_gpu(d2, cfg.P, order=order)
-    o = oracle.Oracle.for_cfg(cfg)
-    parent, row = o.assign(data["K"], data["codebook"])
-    assert np.array_equal(g["row"], row)
-    vsum, counts = o.aggregate(data["V"], parent, row)
-    assert np.array_equal(g["counts"], counts)
-    rng = np.random.default_rng(8)
-    bq = cfg.block_q
-    picks = [(int(rng.integers(cfg.BH)), int(rng.integers(cfg.tiles))) for _ in range(32)] + [(cfg.BH - 1, cfg.tiles - 1)]
-    for bh, t in picks:
-        h = bh % cfg.H
-        rows = order[t * bq:(t + 1) * bq]
-        Qt = d2["Q"][bh:bh + 1, rows]
-        os_ = oracle.Oracle(1, 1, len(rows), cfg.d, cfg.M0, cfg.C)
-        cbh = data["codebook"][h:h + 1]
-        w = os_.importance(Qt, cbh, counts[bh:bh + 1], bq, cfg.scale)
-        sel = os_.select(w, cfg.P)
-        assert np.array_equal(g["sel"][bh, t], sel[0, 0]), (bh, t)
-        Y = os_.attention_substituted(Qt, cbh, vsum[bh:bh + 1], counts[bh:bh + 1], sel, cfg.P, bq, cfg.scale)
-        compare_y(g["Y"][bh:bh + 1, rows], Y, cfg.dtype, f"grid128 Gilbert bh{bh} tile{t}")
+    _ordered_check(_place_along(data, order), data["cfg"].P, order)
 
 
 
@@ -339,7 +348,6 @@ def _decisive_check(data, P, scale, where):
     assert np.array_equal(g["counts"], counts)
     vabs, _ = o.aggregate(np.abs(data["V"].astype(np.float64)), parent, row)
     check_vsum(g["vsum"], vsum, vabs, counts)
-    w = o.importance(data["Q"], data["codebook"], counts, bq, scale)
     w64 = o.importance(data["Q"], data["codebook"], counts, bq, scale)
     werr = np.abs(g["importance"].astype(np.float64) - w64).max()
     say(f"  importance max|err| = {werr:.3e}")
@@ -348,9 +356,10 @@ def _decisive_check(data, P, scale, where):
         srt = -np.sort(-w64, axis=-1)
         margin = (srt[..., P - 1] - srt[..., P]) / np.maximum(srt[..., P - 1], 1.0)
         decisive = (margin >= 1e-4) | ((srt[..., P - 1] == 0.0) & (srt[..., P] == 0.0))
-        sel = o.select(w, P)
+        sel = o.select(w64, P)
         say(f"  decisive tiles {decisive.mean() * 100:.1f}%")
         assert np.array_equal(g["sel"][decisive], sel[decisive])
+        check_topp(g["sel"], g["importance"], w64, P, where)
         sel = g["sel"]
     else:
         sel = np.zeros((cfg.BH, (cfg.N + bq - 1) // bq, 0), np.int32)
