@@ -160,7 +160,7 @@ constexpr int kYRow = 36;  // floats per staged output row (32 dims + 4 to sprea
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
   const size_t pes = dtype == 0 ? 4 : 2;
   const size_t M0p = attn_parent_rows(M0);
-  const size_t W = C <= 8 ? 8 : 16;
+  const size_t W = C == 0 ? 0 : C <= 8 ? 8 : 16;  // a flat codebook has no child fragments
   const size_t per = align256((M0p * d + (size_t)M0 * W * d) * pes);
   return align256((size_t)BH * 4) + (size_t)BH * per;
 }
@@ -202,8 +202,8 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   const int Mt = M0 * (1 + C);
   const int M0p = attn_parent_rows(M0);
   const float* vs = vsum + (int64_t)bh * Mt * D;
-  const int nP = (M0p / 32) * KV * 2 * D;  // parent fragments
-  const int nF = nP + M0 * (W / E) * D;    // + child fragments
+  const int nP = (M0p / 32) * KV * 2 * D;           // parent fragments
+  const int nF = nP + (C > 0 ? M0 * (W / E) * D : 0);  // + child fragments
   // gathers of this thread's fragments (unscaled)
   float x[kPrepFrag][E];
 #pragma unroll
@@ -349,7 +349,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const pvfrag_t* cvf = pvf + nblkP * FV;
   // descriptors of the head's codebook and of the child value fragments
   const __amdgpu_buffer_rsrc_t cb_rs = __builtin_amdgcn_make_buffer_rsrc((void*)cbh, 0, Mt * D * (int)sizeof(in_t), kBufWord3);
-  const __amdgpu_buffer_rsrc_t cv_rs = __builtin_amdgcn_make_buffer_rsrc((void*)cvf, 0, M0 * (W / E) * D * BV, kBufWord3);
+  const __amdgpu_buffer_rsrc_t cv_rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)cvf, 0, C > 0 ? M0 * (W / E) * D * BV : 0, kBufWord3);
   const int nPT = (M0 + 63) / 64;
 
   // ---- once per workgroup: parents into LDS -----------------------------------
@@ -852,7 +853,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   {
     constexpr int E = T::E, KV = 16 / E;
     const int M0p = attn_parent_rows(M0);
-    const int nF = (M0p / 32) * KV * 2 * D + M0 * (W / E) * D;
+    const int nF = (M0p / 32) * KV * 2 * D + (C > 0 ? M0 * (W / E) * D : 0);
     const int per_part = kPrepThreads * kPrepFrag;
     const int parts = std::max(8, (nF + per_part - 1) / per_part);
     hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, BH, M0,
