@@ -20,7 +20,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "avq.h")
 AVQ_F32 = 0
 AVQ_BF16 = 1
 STATUS = {0: "AVQ_OK", -1: "AVQ_ERR_NULL", -2: "AVQ_ERR_SHAPE", -3: "AVQ_ERR_DTYPE", -4: "AVQ_ERR_ALIGN",
-          -5: "AVQ_ERR_UNSUPPORTED", -6: "AVQ_ERR_HIP", -7: "AVQ_ERR_WORKSPACE"}
+          -5: "AVQ_ERR_UNSUPPORTED", -6: "AVQ_ERR_HIP", -7: "AVQ_ERR_WORKSPACE", -8: "AVQ_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 8 << 20  # AVQ_NOALLOC_SCRATCH_BYTES
 
 
 class AvqError(RuntimeError):
@@ -46,6 +47,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avq_attention_fwd_ordered.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, i32, P, P, P, P,
                                                                       ctypes.c_size_t, P]
     lib.avq_attention_fwd_ordered.restype = i32
+    lib.avq_attention_fwd_noalloc.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P]
+    lib.avq_attention_fwd_noalloc.restype = i32
     lib.avq_codebook_update.argtypes = [P, P] + [i32] * 5 + [f32, P, P, P, P]
     lib.avq_codebook_update.restype = i32
     lib.avq_attention_workspace_size.argtypes = [i32] * 6
@@ -245,6 +248,34 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
     if rc != 0:
         raise AvqError(rc, name)
     return Y, topp, imp
+
+
+def attention_fwd_noalloc(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, counts: torch.Tensor, C: int,
+                          P: int, block_q: int, scale: Optional[float] = None, *, Y: torch.Tensor,
+                          topp: Optional[torch.Tensor] = None, importance: Optional[torch.Tensor] = None):
+    """avq_attention_fwd_noalloc: kernel 2 with its operands in the library's static scratch (no
+    workspace).  Every output is caller-provided (Y [B, H, N, d] float32; topp [B, H, T, P] int32 and
+    importance [B, H, T, M0] float32, or None), so this call allocates nothing."""
+    B, H, N, d = _shape4(Q, "Q")
+    Mt, M0 = _codebook_rows(codebook, H, d, Q.dtype, C)
+    T = (N + block_q - 1) // block_q if block_q > 0 else 0
+    _check(vsum, "vsum", (B, H, Mt, d), torch.float32)
+    _check(counts, "counts", (B, H, Mt), torch.int32)
+    _check(Y, "Y", (B, H, N, d), torch.float32)
+    if topp is not None:
+        _check(topp, "topp", (B, H, T, P), torch.int32)
+    if importance is not None:
+        _check(importance, "importance", (B, H, T, M0), torch.float32)
+    _on_device([("Q", Q), ("codebook", codebook), ("vsum", vsum), ("counts", counts), ("Y", Y), ("topp", topp),
+                ("importance", importance)])
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    rc = _lib.avq_attention_fwd_noalloc(_ptr(Q), _ptr(codebook), _ptr(vsum), _ptr(counts), B, H, N, d, M0, C,
+                                        _dtype_code(Q), P, block_q, float(scale), _ptr(Y), _ptr(topp),
+                                        _ptr(importance), _stream(Q))
+    if rc != 0:
+        raise AvqError(rc, "avq_attention_fwd_noalloc")
+    return Y, topp, importance
 
 
 def forward(Q, K, V, codebook, C: int, P: int, block_q: int, scale: Optional[float] = None):

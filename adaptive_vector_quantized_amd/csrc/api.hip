@@ -95,7 +95,7 @@ namespace {
 int attention_call(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H, int N,
                    int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
                    float* importance, void* workspace, size_t workspace_bytes, void* stream, bool approx,
-                   const int32_t* order, bool ordered) {
+                   const int32_t* order, bool ordered, bool validate_only = false) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
   if (P < 0 || P > M0 || (C == 0 && P > 0)) return AVQ_ERR_SHAPE;  // no children to refine with
@@ -111,6 +111,7 @@ int attention_call(const void* Q, const void* codebook, const float* vsum, const
   if (workspace_bytes < avq::attention_workspace_bytes(dtype, d, M0, C, (int)BH)) return AVQ_ERR_WORKSPACE;
   if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q, importance != nullptr) > (size_t)kMaxLds)
     return AVQ_ERR_UNSUPPORTED;
+  if (validate_only) return AVQ_OK;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
                                         Y, topp, importance, workspace, approx, order, (hipStream_t)stream));
 }
@@ -142,6 +143,58 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                         workspace, workspace_bytes, stream, approx_denominator != 0, query_order, true);
 }
 
+}  // extern "C"
+
+// ---- the attention call without a caller workspace --------------------------
+// Scratch for avq_attention_fwd_noalloc: the operands avq_attention_fwd keeps
+// in its workspace (a value scale per (batch, head) and the value sums as fp16
+// fragments), in a static array every GPU the library runs on holds from the
+// library's load to the end of the process.  Host code never uses the array's
+// name as an address: its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[AVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// device address of this GPU's scratch (the current device), or nullptr
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int avq_attention_fwd_noalloc(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B,
+                              int H, int N, int d, int M0, int C, int dtype, int P, int block_q, float scale,
+                              float* Y, int32_t* topp, float* importance, void* stream) {
+  // the arguments of avq_attention_fwd are checked first (with a stand-in
+  // workspace of the right size, so only the scratch limit is left)
+  const size_t need = avq_attention_workspace_size(B, H, d, M0, C, dtype);
+  static unsigned char probe[16] __attribute__((aligned(16)));
+  int rc = attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp,
+                          importance, probe, need, stream, false, nullptr, false, /*validate_only=*/true);
+  if (rc != AVQ_OK) return rc;
+  if ((int64_t)B * H == 0 || N == 0) return AVQ_OK;
+  if (need > (size_t)AVQ_NOALLOC_SCRATCH_BYTES) return AVQ_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (ws == nullptr) return AVQ_ERR_HIP;
+  return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
+                        ws, need, stream, false, nullptr, false, false);
+}
+
 int avq_codebook_update(const float* ksum, const int32_t* counts, int B, int H, int d, int M0, int C, float decay,
                         float* S, float* Nema, float* codebook, void* stream) {
   if (B < 0 || H < 0 || d < 1 || M0 < 1 || C < 0) return AVQ_ERR_SHAPE;
@@ -165,6 +218,7 @@ const char* avq_status_string(int status) {
     case AVQ_ERR_UNSUPPORTED: return "unsupported size (d, M0, C, block_q, B*H or H*M0)";
     case AVQ_ERR_HIP: return "HIP runtime error";
     case AVQ_ERR_WORKSPACE: return "workspace smaller than avq_attention_workspace_size()";
+    case AVQ_ERR_SCRATCH: return "the call needs more than the library's static scratch (AVQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

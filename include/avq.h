@@ -64,6 +64,10 @@ extern "C" {
 #define AVQ_ERR_UNSUPPORTED (-5) /* valid but unsupported (d, M0, C, block_q) */
 #define AVQ_ERR_HIP (-6)         /* the HIP runtime reported an error */
 #define AVQ_ERR_WORKSPACE (-7)   /* workspace missing or too small */
+#define AVQ_ERR_SCRATCH (-8)     /* more than avq_attention_fwd_noalloc's static scratch */
+
+/* Size of the static device scratch behind avq_attention_fwd_noalloc (per GPU). */
+#define AVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 #define AVQ_F32 0
 #define AVQ_BF16 1
@@ -218,6 +222,35 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                               const int32_t* query_order, int approx_denominator,
                               float* Y, int32_t* topp, float* importance,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * avq_attention_fwd without a workspace argument, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  It computes exactly what
+ * avq_attention_fwd computes, with the same kernels, arguments (minus
+ * workspace and workspace_bytes), layouts and errors, and allocates nothing:
+ * the operands avq_attention_fwd keeps in its workspace live in a static
+ * device array of AVQ_NOALLOC_SCRATCH_BYTES (8 MiB) that every GPU the
+ * library runs on holds from the library's load to the end of the process.
+ * Its address on a GPU is looked up on the first call made with that GPU
+ * current.
+ *
+ * Limit: calls whose avq_attention_workspace_size() exceeds
+ * AVQ_NOALLOC_SCRATCH_BYTES return AVQ_ERR_SCRATCH and write nothing (bf16,
+ * d = 64, M0 = 64, C = 8 fits B*H <= 113; d = 128, M0 = 256, C = 8 fits
+ * B*H <= 14).
+ *
+ * Concurrency: every call on one GPU uses that GPU's one scratch array, and
+ * each call overwrites what it uses before reading it (nothing carries over
+ * from an earlier call).  Calls on one GPU must therefore not overlap: two
+ * calls in flight at once -- on different streams, or from different host
+ * threads -- race on the scratch and give wrong results.  Calls on one stream
+ * run one after another and are safe.
+ */
+int avq_attention_fwd_noalloc(const void* Q, const void* codebook, const float* vsum,
+                              const int32_t* counts, int B, int H, int N, int d, int M0,
+                              int C, int dtype, int P, int block_q, float scale,
+                              float* Y, int32_t* topp, float* importance, void* stream);
 
 /*
  * Codebook update step of the training recipe (App. A, Eq. 11 and Eq. 12;

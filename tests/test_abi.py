@@ -22,8 +22,8 @@ def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
     assert set(names) == {"avq_assign_aggregate", "avq_assign_aggregate_kv", "avq_attention_fwd", "avq_attention_fwd_approx",
-                          "avq_attention_fwd_ordered", "avq_attention_workspace_size", "avq_codebook_update",
-                          "avq_status_string", "avq_version"}
+                          "avq_attention_fwd_ordered", "avq_attention_fwd_noalloc", "avq_attention_workspace_size",
+                          "avq_codebook_update", "avq_status_string", "avq_version"}
     for n in names:
         assert hasattr(L, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
@@ -33,8 +33,8 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_strings(L):
     assert L.avq_version() == 100
-    for code in range(0, -8, -1):
-        assert L.avq_status_string(code)
+    for code in range(0, -9, -1):
+        assert L.avq_status_string(code) != b"unknown status"
 
 
 def _buf(n=64):
@@ -60,6 +60,10 @@ def _call_attn(L, fn="avq_attention_fwd", **kw):
     a = dict(Q=p, cb=p, vsum=p, counts=p, B=1, H=1, N=8, d=64, M0=4, C=2, dtype=1, P=2, bq=64, scale=0.125,
              Y=p, topp=None, imp=None, ws=p, wsb=1 << 30, order=p, approx=0)
     a.update(kw)
+    if fn == "avq_attention_fwd_noalloc":
+        return L.avq_attention_fwd_noalloc(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"],
+                                           a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"],
+                                           a["topp"], a["imp"], None)
     if fn == "avq_attention_fwd_ordered":
         return L.avq_attention_fwd_ordered(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"],
                                            a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["order"],
@@ -97,7 +101,8 @@ def test_assign_validation(L, kv):
         assert _assign(L, ksum=mis) == -4
 
 
-@pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx", "avq_attention_fwd_ordered"])
+@pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx", "avq_attention_fwd_ordered",
+                                "avq_attention_fwd_noalloc"])
 def test_attention_validation(L, fn):
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 8)
@@ -119,11 +124,18 @@ def test_attention_validation(L, fn):
     assert _attn(L, Y=mis) == -4
     assert _attn(L, topp=mis) == -4
     assert _attn(L, scale=0.0) == -2
-    assert _attn(L, ws=None) == -1
-    assert _attn(L, ws=mis) == -4
-    need = L.avq_attention_workspace_size(1, 1, 64, 4, 2, 1)
-    assert need > 0
-    assert _attn(L, wsb=need - 1) == -7
+    if fn != "avq_attention_fwd_noalloc":
+        assert _attn(L, ws=None) == -1
+        assert _attn(L, ws=mis) == -4
+        need = L.avq_attention_workspace_size(1, 1, 64, 4, 2, 1)
+        assert need > 0
+        assert _attn(L, wsb=need - 1) == -7
+    else:
+        # beyond the static scratch: refused before anything is launched
+        need = L.avq_attention_workspace_size(1, 200, 64, 64, 8, 1)
+        assert need > (8 << 20)
+        assert _attn(L, H=200, M0=64, C=8, P=16, bq=128) == -8
+        assert L.avq_attention_workspace_size(1, 113, 64, 64, 8, 1) <= (8 << 20)
     assert L.avq_attention_workspace_size(1, 1, 96, 4, 2, 1) == 0   # invalid sizes
     assert _attn(L, N=0) == 0         # no queries: nothing to do
     assert _attn(L, B=0, Q=None) == 0
