@@ -807,6 +807,487 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   }
 }
 
+// ---- software-pipelined kernel for at most 64 parents (bf16, d = 64, P > 0) --
+// The same arithmetic as attention_kernel with all parents in LDS, with the
+// tile loop reordered so that the waits of one tile overlap the work of the
+// next: while the children of tile t are being copied into LDS, every wave
+// runs the parent pass of tile t + 1 (its weighted values go to a second set
+// of accumulators), and the next queries are loaded as soon as the current
+// ones are dead.  The children of a whole tile (up to kPipeBlocks 32-row
+// blocks) are staged at once, so a tile takes two workgroup barriers: one
+// after which the staged children (and the next tile's importance partials)
+// are visible, one after which every wave is done with them.  Per tile t:
+//   (a) parent pass of t + 1, importance partials of t + 1
+//   (b) wait for this wave's copies; barrier
+//   (c) children of t (later stages, when P needs more than kPipeBlocks
+//       blocks, are copied and waited for in place); load the queries of t + 2
+//   (d) top-P of t + 1
+//   (h) output of t
+//   (e) barrier; (f) copy the children of t + 1, load their counts
+// The parents' logits start their MFMA accumulation from the parents' bias
+// (0, or -inf for a parent without keys), so the mask costs no instruction.
+// Children are masked only when needed: their logits' unmasked maximum is
+// formed first, and only if it exceeds the stabiliser by more than the lazy
+// margin (a rare event) are empty children masked out of the maximum.
+// Otherwise every child weight is at most 2^8, and the children that must not
+// contribute (no keys, padding rows, slots past P) carry exactly zero values
+// and counts, so they add nothing.
+constexpr int kPipeBlocks = 4;
+
+size_t attention_pipe_smem_bytes(int d, int P, int block_q) {
+  const size_t es = 2;  // bf16 codewords, fp16 value fragments
+  const size_t nw = block_q / 32;
+  size_t b = 2 * (size_t)64 * d * es;             // parents' codeword and value fragments
+  b += 2 * (size_t)kPipeBlocks * 32 * d * es;     // staged children's codeword and value fragments
+  b += 2 * 64 * 4 + 2 * kPipeBlocks * 32 * 4;     // counts and biases
+  b += 64 * 4 * 4;                                // importance partials
+  b += nw * (size_t)P * 4 + 16;                   // selections, flags
+  b = (b + 15) & ~(size_t)15;
+  b += nw * 32 * kYRow * 4;                       // output staging
+  return b;
+}
+
+template <class T, int D, int W>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attention_pipe_kernel(
+    const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
+    const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
+    int bq, int tiles_per_wg, int wgs_per_bh, float sl2, float* __restrict__ Y, int* __restrict__ topp,
+    float* __restrict__ importance, const int* __restrict__ order) {
+  using in_t = typename T::in_t;
+  using frag_t = typename T::frag_t;
+  using pvfrag_t = typename T::pvfrag_t;
+  constexpr int E = T::E;
+  constexpr int KS = D / (2 * E);
+  constexpr int DB = D / 32;
+  constexpr int S = 32 / W;
+  constexpr int KV = 16 / E;
+  constexpr int FA = KS * 64;
+  constexpr int FV = KV * 2 * D;
+  constexpr int BA = (int)sizeof(frag_t);
+  constexpr int BV = (int)sizeof(pvfrag_t);
+  constexpr int SB = kPipeBlocks;
+  constexpr float kLazy = 8.0f;
+  static_assert(SB % 2 == 0, "children are processed two blocks at a time");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nw = blockDim.x >> 6;
+  const int Mt = M0 * (1 + C);
+  const int nCB = ((P + S - 1) / S + 1) & ~1;  // child blocks of a tile, even
+  const int nStage = (nCB + SB - 1) / SB;
+  frag_t* sPC = (frag_t*)smem;                        // [2 * FA]
+  pvfrag_t* sPV = (pvfrag_t*)(sPC + 2 * FA);          // [2 * FV]
+  frag_t* sCC = (frag_t*)(sPV + 2 * FV);              // [SB * FA]
+  pvfrag_t* sCV = (pvfrag_t*)(sCC + SB * FA);         // [SB * FV]
+  float* sNp = (float*)(sCV + SB * FV);               // [64] parent counts, by value column
+  float* sBp = sNp + 64;                              // [64] 0 or -inf
+  float* sNc = sBp + 64;                              // [SB * 32] staged children's counts, by column
+  float* sBc = sNc + SB * 32;                         // [SB * 32] 0 or -inf
+  float* sW = sBc + SB * 32;                          // [64][4] importance partials per wave
+  int* sSel = (int*)(sW + 256);                       // [nw][P] selection (every wave its own copy)
+  int* sFlag = sSel + nw * P;                         // [0] stage has rows to mask
+  float* sY = (float*)(smem + ((((unsigned char*)(sFlag + 4) - smem) + 15) & ~15));  // [nw][32][kYRow]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ql = lane & 31, hh = lane >> 5;
+  int bh, g;
+  {
+    const int L = blockIdx.x;
+    if ((BH & 7) == 0) {
+      const int k = L >> 3;
+      bh = (k / wgs_per_bh) * 8 + (L & 7);
+      g = k % wgs_per_bh;
+    } else {
+      bh = L / wgs_per_bh;
+      g = L % wgs_per_bh;
+    }
+  }
+  const int h = bh % H;
+  const int ntiles = (N + bq - 1) / bq;
+  const int tile0 = g * tiles_per_wg;
+  const int tile1 = min(ntiles, tile0 + tiles_per_wg);
+  if (tile0 >= tile1) return;
+  const in_t* cbh = cb + (int64_t)h * Mt * D;
+  const int* nb = counts + (int64_t)bh * Mt;
+  const in_t* Qb = Q + (int64_t)bh * N * D;
+  float* Yb = Y + (int64_t)bh * N * D;
+  const float sig = ((const float*)ws)[bh];
+  const pvfrag_t* pvf = (const pvfrag_t*)(ws + sig_bytes + (size_t)bh * per_bh);
+  const pvfrag_t* cvf = pvf + 2 * FV;
+  const __amdgpu_buffer_rsrc_t cb_rs = __builtin_amdgcn_make_buffer_rsrc((void*)cbh, 0, Mt * D * (int)sizeof(in_t), kBufWord3);
+  const __amdgpu_buffer_rsrc_t cv_rs = __builtin_amdgcn_make_buffer_rsrc((void*)cvf, 0, M0 * (W / E) * D * BV, kBufWord3);
+  const float sl2C = sl2 / (float)C;  // Eq. 8's mean folded into the logit scale
+
+  // ---- once per workgroup: parents into LDS -------------------------------------
+  for (int u = wave; u < 2 * KS; u += nw) {
+    const int b = u / KS, s = u % KS;
+    const int j = b * 32 + ql;
+    lds_dma<BA>(cbh + (int64_t)(j < M0 ? j : 0) * D + s * 2 * E + E * hh, sPC + u * 64);
+  }
+  for (int u = wave; u < 2 * FV / 64; u += nw) lds_dma<BV>(pvf + u * 64 + lane, sPV + u * 64);
+  // importance partials: slots of absent waves and of parents past M0 stay zero
+  for (int i = tid; i < 256; i += blockDim.x) sW[i] = 0.0f;
+  if (tid < 64) {
+    const int j = parent_of_col(tid);
+    const float n = j < M0 ? (float)nb[j] : 0.0f;
+    sNp[tid] = n;
+    sBp[tid] = n > 0.0f ? 0.0f : -INFINITY;
+  }
+
+  // queries: rows of tile positions (an order gathers them; entries are
+  // fetched a tile ahead of the loads that use them)
+  auto order_at = [&](int pos) -> int { return (order != nullptr && pos < N) ? order[pos] : pos; };
+  auto query_row = [&](int pos, int entry) -> int {
+    if (pos >= N) return -1;
+    if (order == nullptr) return pos;
+    return (entry >= 0 && entry < N) ? entry : -1;
+  };
+  auto load_q = [&](frag_t (&qq)[KS], int row) {
+    const in_t* qp = Qb + (int64_t)(row >= 0 ? row : 0) * D + E * hh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qq[s] = *(const frag_t*)(qp + s * 2 * E);
+  };
+  auto qpos = [&](int t) { return t * bq + wave * 32 + ql; };
+
+  float* yw = sY + wave * 32 * kYRow;
+  auto store_rows = [&](int q0, int db, int row) {
+    __builtin_amdgcn_wave_barrier();
+    const int r0 = lane >> 3, c4 = (lane & 7) * 4;
+    const float* src = yw + r0 * kYRow + c4;
+    if (order != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = __shfl(row, r0 + 8 * k);
+        if (r >= 0)
+          __builtin_nontemporal_store(*(const f32x4*)(src + 8 * k * kYRow), (f32x4*)(Yb + (int64_t)r * D + db * 32 + c4));
+      }
+      return;
+    }
+    float* dst = Yb + (int64_t)(q0 + r0) * D + db * 32 + c4;
+    if (q0 + 32 <= N) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) __builtin_nontemporal_store(*(const f32x4*)(src + 8 * k * kYRow), (f32x4*)(dst + 8 * k * D));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (q0 + r0 + 8 * k < N)
+          __builtin_nontemporal_store(*(const f32x4*)(src + 8 * k * kYRow), (f32x4*)(dst + 8 * k * D));
+    }
+  };
+
+  // Parent pass of one tile (Alg. 2, Eq. 6; Eq. 18 with its lazy stabiliser)
+  // and, from the weights still in registers, this wave's importance
+  // partials (Eq. 7) in sW.
+  auto parent_pass = [&](const frag_t (&qq)[KS], bool qv, f32x16 (&xa)[DB], float& zz, float& mm) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) xa[db] = zero16();
+    f32x16 lg[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x4* bp = (const f32x4*)(sBp + b * 32 + 8 * hh);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lg[b][q * 4 + u] = b4[u];
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(b * KS + s) * 64 + lane], qq[s], lg[b]);
+    }
+    float tm = -INFINITY;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tm = fmaxf(tm, lg[b][r]);
+    // the first (only) pass: the accumulators are zero, no rescaling
+    mm = fmaxf(xhalf_max(tm) * sl2, -FLT_MAX);
+    float z = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x4* np4 = (const f32x4*)(sNp + b * 32 + 8 * hh);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 n4 = np4[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float a = fast_exp2(fmaf(lg[b][q * 4 + u], sl2, -mm));
+          lg[b][q * 4 + u] = a;
+          z = fmaf(a, n4[u], z);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KV; ++k) {
+        const pvfrag_t bf = pv_operand<T, KV>(lg[b], k);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          xa[db] = T::mma_pv(sPV[((b * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xa[db]);
+      }
+    }
+    zz = z;
+    // Eq. 7: A / z summed over the wave's 32 queries; the count n_j is a
+    // factor of the whole sum, applied after the reduction
+    const float rz = qv ? 1.0f / xhalf_sum(z) : 0.0f;
+    float t[32];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * rz;
+    rs_half32(t, lane);
+    const int j = 32 * (ql >> 4) + row_of(ql & 15, hh);
+    if (j < M0) sW[j * 4 + wave] = t[0] * sNp[32 * (ql >> 4) + col_of(ql & 15, hh)];
+  };
+
+  // Top-P of one tile (Alg. 2, the parent choice) from the importance
+  // partials of every wave; every wave forms its own copy of the selection.
+  auto top_p = [&](int tile) {
+    uint32_t u1[1];
+    {
+      const f32x4 p4 = *(const f32x4*)(sW + lane * 4);
+      u1[0] = lane < M0 ? __float_as_uint((p4[0] + p4[1]) + (p4[2] + p4[3])) : 0u;
+    }
+    if (importance && wave == 0 && lane < M0)
+      importance[((int64_t)bh * ntiles + tile) * M0 + lane] = __uint_as_float(u1[0]);
+    int* gout = (topp && wave == 0) ? topp + ((int64_t)bh * ntiles + tile) * P : nullptr;
+    select_top<1>(u1, M0, P, lane, sSel + wave * P, gout);
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  // Copies of one stage of the selected parents' children into LDS (this
+  // wave's share): codeword fragments, value fragments.  Slots past P and
+  // rows past C read zeros (offsets out of range).
+  const int r_row = r_of_row(ql), h_row = h_of_row(ql);
+  const int s_row = 2 * (r_row / W) + h_row, c_row = r_row % W;
+  auto stage_issue = [&](int st) {
+    const int* sel = sSel + wave * P;
+    const int b0 = st * SB;
+    const int nb_st = min(SB, nCB - b0);
+    for (int u = wave; u < nb_st * KS; u += nw) {
+      const int b = u / KS, s = u % KS;
+      const int gs = (b0 + b) * S + s_row;
+      const bool ok = gs < P && c_row < C;
+      const int voff = ((M0 + sel[ok ? gs : 0] * C + c_row) * D + s * 2 * E + E * hh) * (int)sizeof(in_t);
+      lds_dma_buf<BA>(cb_rs, ok ? voff : kOutOfRange, sCC + u * 64);
+    }
+    for (int u = wave; u < nb_st * KV * 2 * (D / 64); u += nw) {
+      const int dc = u % (D / 64), t = u / (D / 64);
+      const int h2 = t % 2, bk = t / 2, k = bk % KV, b = bk / KV;
+      const int r = k * E;
+      const int gs = (b0 + b) * S + 2 * (r / W) + h2, gg = (r % W) / E;
+      const int voff = gs < P ? ((sel[gs] * (W / E) + gg) * D + dc * 64 + lane) * BV : kOutOfRange;
+      lds_dma_buf<BV>(cv_rs, voff, sCV + ((b * KV + k) * 2 + h2) * D + dc * 64);
+    }
+  };
+  // counts of one stage's rows (wave 0; two rows per lane), loaded into
+  // registers here and written to LDS by stage_counts_store
+  auto stage_counts_load = [&](int st, int (&cn)[SB / 2]) {
+    const int* sel = sSel;  // wave 0's copy
+#pragma unroll
+    for (int i = 0; i < SB / 2; ++i) {
+      const int row = lane + 64 * i;
+      const int b = st * SB + (row >> 5), qq = row & 31;
+      const int r = r_of_col(qq), hc = h_of_col(qq);
+      const int gs = b * S + 2 * (r / W) + hc, cc = r % W;
+      cn[i] = (gs < P && cc < C) ? nb[M0 + sel[gs] * C + cc] : 0;
+    }
+  };
+  auto stage_counts_store = [&](const int (&cn)[SB / 2]) {
+    bool any_empty = false;
+#pragma unroll
+    for (int i = 0; i < SB / 2; ++i) {
+      const float n = (float)cn[i];
+      sNc[lane + 64 * i] = n;
+      sBc[lane + 64 * i] = n > 0.0f ? 0.0f : -INFINITY;
+      any_empty = any_empty || !(n > 0.0f);
+    }
+    const bool e = __builtin_amdgcn_ballot_w64(any_empty) != 0;
+    if (lane == 0) sFlag[0] = e ? 1 : 0;
+  };
+
+  // The children of one staged stage (Alg. 2, the refinement loop; Eq. 8-9),
+  // two 32-row blocks at a time, into the accumulators of the tile.
+  auto children_stage = [&](int st, const frag_t (&qq)[KS], f32x16 (&xa)[DB], float& zz, float& mm) {
+    const bool stage_masked = __builtin_amdgcn_readfirstlane(sFlag[0]) != 0;
+    const int nb_st = min(SB, nCB - st * SB);
+    for (int pb = 0; pb < nb_st; pb += 2) {
+      f32x16 cl[2];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        cl[bb] = zero16();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cl[bb] = T::mma_in(sCC[((pb + bb) * KS + s) * 64 + lane], qq[s], cl[bb]);
+      }
+      // Eq. 8: the parent logit is the mean of its C child logits, taken
+      // before any masking (padding rows have zero codewords)
+      float sp[2][16 / W];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int g2 = 0; g2 < 16 / W; ++g2) {
+          float acc = cl[bb][g2 * W];
+#pragma unroll
+          for (int c = 1; c < W; ++c) acc += cl[bb][g2 * W + c];
+          sp[bb][g2] = acc;
+        }
+      float tm = -INFINITY;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tm = fmaxf(tm, cl[bb][r]);
+      tm = xhalf_max(tm) * sl2;
+      if (__builtin_amdgcn_ballot_w64(tm > mm + kLazy) != 0) {
+        // rare: a child logit exceeds the stabiliser by more than the lazy
+        // margin; Eq. 18 takes the maximum over children with keys only
+        if (stage_masked) {
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            const f32x4* bc = (const f32x4*)(sBc + (pb + bb) * 32 + 8 * hh);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 b4 = bc[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) cl[bb][q * 4 + u] += b4[u];
+            }
+          }
+          tm = -INFINITY;
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tm = fmaxf(tm, cl[bb][r]);
+          tm = xhalf_max(tm) * sl2;
+        }
+        if (tm > mm + kLazy) {
+          const float f = fast_exp2(mm - tm);
+          zz *= f;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) xa[db] *= f;
+          mm = tm;
+        }
+      }
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const f32x4* nc = (const f32x4*)(sNc + (pb + bb) * 32 + 8 * hh);
+#pragma unroll
+        for (int g2 = 0; g2 < 16 / W; ++g2) {
+          const bool slot_ok = (st * SB + pb + bb) * S + 2 * g2 + hh < P;
+          const float ap = slot_ok ? fast_exp2(fminf(fmaf(sp[bb][g2], sl2C, -mm), kLazy + 1.0f)) : 0.0f;
+#pragma unroll
+          for (int q = (g2 * W) / 4; q < (g2 * W + W) / 4; ++q) {
+            const f32x4 n4 = nc[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float da = fast_exp2(fmaf(cl[bb][q * 4 + u], sl2, -mm)) - ap;
+              cl[bb][q * 4 + u] = da;
+              zz = fmaf(da, n4[u], zz);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+          const pvfrag_t bf = pv_operand<T, KV>(cl[bb], k);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            xa[db] = T::mma_pv(sCV[(((pb + bb) * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xa[db]);
+        }
+      }
+    }
+  };
+
+  // children of a tile: stage 0 is staged already; later stages are copied
+  // and waited for here
+  auto children = [&](const frag_t (&qq)[KS], f32x16 (&xa)[DB], float& zz, float& mm) {
+    children_stage(0, qq, xa, zz, mm);
+    for (int st = 1; st < nStage; ++st) {
+      lds_barrier();  // every wave is done with the previous stage
+      stage_issue(st);
+      if (wave == 0) {
+        int cn[SB / 2];
+        stage_counts_load(st, cn);
+        stage_counts_store(cn);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
+      children_stage(st, qq, xa, zz, mm);
+    }
+  };
+
+  // Y = x / z (Alg. 2, the final normalisation), through LDS 32 dims at a time
+  auto output = [&](int tile, const f32x16 (&xa)[DB], float zz, bool qv, int qrow_t) {
+    const float zt = xhalf_sum(zz);
+    const float f = qv ? sig / zt : 0.0f;
+    const int q0 = tile * bq + wave * 32;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x16& a = xa[db];
+        const f32x4 o = {a[4 * i] * f, a[4 * i + 1] * f, a[4 * i + 2] * f, a[4 * i + 3] * f};
+        *(f32x4*)(yw + ql * kYRow + 8 * i + 4 * hh) = o;
+      }
+      store_rows(q0, db, qrow_t);
+    }
+  };
+
+  // ---- prologue: tile0's parent pass, selection and child copies ----------------
+  frag_t qA[KS], qB[KS];
+  f32x16 xA[DB], xB[DB];
+  float zA = 0.0f, mA = -FLT_MAX, zB = 0.0f, mB = -FLT_MAX;
+  int rowA = query_row(qpos(tile0), order_at(qpos(tile0)));
+  int rowB = -1;
+  int entry_n = order_at(qpos(tile0 + 1));  // order entry of this lane's query in the next tile
+  load_q(qA, rowA);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  parent_pass(qA, rowA >= 0, xA, zA, mA);
+  if (tile0 + 1 < tile1) {
+    rowB = query_row(qpos(tile0 + 1), entry_n);
+    load_q(qB, rowB);
+    entry_n = order_at(qpos(tile0 + 2));
+  }
+  lds_barrier();  // importance partials of tile0
+  top_p(tile0);
+  int cnt[SB / 2];
+  lds_barrier();  // every wave has read the partials
+  stage_issue(0);
+  if (wave == 0) stage_counts_load(0, cnt);
+
+  // ---- the pipelined tile loop (unrolled by two: the register sets swap roles) --
+  auto step = [&](int t, frag_t (&qc)[KS], f32x16 (&xc)[DB], float& zc, float& mc, int& rowc,
+                  frag_t (&qn)[KS], f32x16 (&xn)[DB], float& zn, float& mn, int& rown) {
+    const bool more = t + 1 < tile1;
+    // (a) the next tile's parent pass and importance partials
+    if (more) parent_pass(qn, rown >= 0, xn, zn, mn);
+    // (b) this wave's copies (and counts) of tile t have landed; barrier
+    if (wave == 0) stage_counts_store(cnt);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    // (c) the children of tile t; then the queries of tile t + 2
+    children(qc, xc, zc, mc);
+    const int rowt = rowc;
+    const bool qvt = rowc >= 0;
+    if (t + 2 < tile1) {
+      rowc = query_row(qpos(t + 2), entry_n);
+      load_q(qc, rowc);
+      entry_n = order_at(qpos(t + 3));
+    }
+    // (d) the next tile's selection
+    if (more) top_p(t + 1);
+    // (h) the output of tile t
+    output(t, xc, zc, qvt, rowt);
+    // (e) every wave is done with tile t's children and the partials; (f) the
+    // next tile's child copies and counts
+    if (more) {
+      lds_barrier();
+      stage_issue(0);
+      if (wave == 0) stage_counts_load(0, cnt);
+    }
+  };
+  for (int t = tile0; t < tile1; t += 2) {
+    step(t, qA, xA, zA, mA, rowA, qB, xB, zB, mB, rowB);
+    if (t + 1 < tile1) step(t + 1, qB, xB, zB, mB, rowB, qA, xA, zA, mA, rowA);
+  }
+}
+
 size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q, bool importance) {
   const size_t es = dtype == 0 ? 4 : 2;   // input and value operand element (same width)
   const size_t M0p = attn_parent_rows(M0);
@@ -861,14 +1342,27 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t smem = attention_smem_bytes(dtype, D, M0, C, P, bq, importance != nullptr);
-  auto kern = attention_kernel<T, D, W, PL, VL>;
-  hipError_t e = raise_lds_limit((const void*)kern, smem);
-  if (e != hipSuccess) return e;
   const int tpw = attention_tiles_per_wg(BH, N, bq);
   const int T_ = (N + bq - 1) / bq;
   const int per = (T_ + tpw - 1) / tpw;
   const float sl2 = scale * 1.4426950408889634f;
+  if constexpr (PL && VL && D == 64 && std::is_same<T, TBF16>::value) {
+    if (P > 0) {
+      // all parents in LDS and children to refine: the pipelined tile loop
+      const size_t smem = attention_pipe_smem_bytes(D, P, bq);
+      auto kern = attention_pipe_kernel<T, D, W>;
+      hipError_t e = raise_lds_limit((const void*)kern, smem);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
+                         (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N,
+                         M0, C, P, bq, tpw, per, sl2, Y, topp, importance, order);
+      return hipGetLastError();
+    }
+  }
+  const size_t smem = attention_smem_bytes(dtype, D, M0, C, P, bq, importance != nullptr);
+  auto kern = attention_kernel<T, D, W, PL, VL>;
+  hipError_t e = raise_lds_limit((const void*)kern, smem);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
                      (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N, M0, C,
                      P, bq, tpw, per, sl2, Y, topp, importance, approx ? 1 : 0, order);
