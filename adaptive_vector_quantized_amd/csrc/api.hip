@@ -92,28 +92,36 @@ size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C, int dtyp
 
 namespace {
 
+// stages: avq::kAttnPrep (value fragments from vsum into the workspace) and/or
+// avq::kAttnKernel (the attention kernel, from a prepared workspace); vsum is
+// needed by the first, Q, codebook, counts and Y by the second
 int attention_call(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H, int N,
                    int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
                    float* importance, void* workspace, size_t workspace_bytes, void* stream, bool approx,
-                   const int32_t* order, bool ordered, bool validate_only = false) {
+                   const int32_t* order, bool ordered, bool validate_only = false,
+                   int stages = avq::kAttnPrep | avq::kAttnKernel) {
+  const bool prep = (stages & avq::kAttnPrep) != 0, kern = (stages & avq::kAttnKernel) != 0;
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
-  if (P < 0 || P > M0 || (C == 0 && P > 0)) return AVQ_ERR_SHAPE;  // no children to refine with
-  if (block_q != 32 && block_q != 64 && block_q != 128) return AVQ_ERR_UNSUPPORTED;
-  if (!isfinite(scale) || !(scale > 0.0f)) return AVQ_ERR_SHAPE;
+  if (kern) {
+    if (P < 0 || P > M0 || (C == 0 && P > 0)) return AVQ_ERR_SHAPE;  // no children to refine with
+    if (block_q != 32 && block_q != 64 && block_q != 128) return AVQ_ERR_UNSUPPORTED;
+    if (!isfinite(scale) || !(scale > 0.0f)) return AVQ_ERR_SHAPE;
+  }
   const int64_t BH = (int64_t)B * H;
-  if (BH == 0 || N == 0) return AVQ_OK;
-  if (!Q || !codebook || !vsum || !counts || !Y || !workspace || (ordered && !order)) return AVQ_ERR_NULL;
-  if (!aligned16(Q) || !aligned16(codebook) || !aligned16(vsum) || !aligned16(counts) || !aligned16(Y) ||
-      !aligned16(workspace) || (topp && !aligned16(topp)) || (importance && !aligned16(importance)) ||
-      ((uintptr_t)order & 3u) != 0)
+  if (BH == 0 || (kern && N == 0)) return AVQ_OK;
+  if (!workspace || (prep && !vsum) || (kern && (!Q || !codebook || !counts || !Y || (ordered && !order))))
+    return AVQ_ERR_NULL;
+  if ((Q && !aligned16(Q)) || (codebook && !aligned16(codebook)) || (vsum && !aligned16(vsum)) ||
+      (counts && !aligned16(counts)) || (Y && !aligned16(Y)) || !aligned16(workspace) || (topp && !aligned16(topp)) ||
+      (importance && !aligned16(importance)) || ((uintptr_t)order & 3u) != 0)
     return AVQ_ERR_ALIGN;
   if (workspace_bytes < avq::attention_workspace_bytes(dtype, d, M0, C, (int)BH)) return AVQ_ERR_WORKSPACE;
-  if (avq::attention_smem_bytes(dtype, d, M0, C, P, block_q, importance != nullptr) > (size_t)kMaxLds)
+  if (kern && avq::attention_smem_bytes(dtype, d, M0, C, P, block_q, importance != nullptr) > (size_t)kMaxLds)
     return AVQ_ERR_UNSUPPORTED;
   if (validate_only) return AVQ_OK;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
-                                        Y, topp, importance, workspace, approx, order, (hipStream_t)stream));
+                                        Y, topp, importance, workspace, approx, order, stages, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -141,6 +149,20 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                               float* importance, void* workspace, size_t workspace_bytes, void* stream) {
   return attention_call(Q, codebook, vsum, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
                         workspace, workspace_bytes, stream, approx_denominator != 0, query_order, true);
+}
+
+int avq_attention_prepare(const float* vsum, int B, int H, int d, int M0, int C, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return attention_call(nullptr, nullptr, vsum, nullptr, B, H, 0, d, M0, C, dtype, 0, 32, 1.0f, nullptr, nullptr, nullptr,
+                        workspace, workspace_bytes, stream, false, nullptr, false, false, avq::kAttnPrep);
+}
+
+int avq_attention_fwd_prepared(const void* Q, const void* codebook, const int32_t* counts, int B, int H, int N, int d,
+                               int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
+                               float* importance, const void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(Q, codebook, nullptr, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
+                        const_cast<void*>(workspace), workspace_bytes, stream, false, nullptr, false, false,
+                        avq::kAttnKernel);
 }
 
 }  // extern "C"

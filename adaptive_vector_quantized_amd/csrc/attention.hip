@@ -1327,11 +1327,11 @@ int attention_tiles_per_wg(int BH, int N, int bq) {
 template <class T, int D, int W, bool PL, bool VL>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, const int* order, hipStream_t st) {
+                                void* ws, bool approx, const int* order, int stages, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
   const size_t sig_bytes = align256((size_t)BH * 4);
   const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
-  {
+  if (stages & kAttnPrep) {
     constexpr int E = T::E, KV = 16 / E;
     const int M0p = attn_parent_rows(M0);
     const int nF = (M0p / 32) * KV * 2 * D + (C > 0 ? M0 * (W / E) * D : 0);
@@ -1342,6 +1342,7 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(stages & kAttnKernel)) return hipSuccess;
   const int tpw = attention_tiles_per_wg(BH, N, bq);
   const int T_ = (N + bq - 1) / bq;
   const int per = (T_ + tpw - 1) / tpw;
@@ -1372,10 +1373,10 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
 template <class T, int D, int W>
 static hipError_t launch_attn_v(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, const int* order, hipStream_t st) {
+                                void* ws, bool approx, const int* order, int stages, hipStream_t st) {
   if (M0 <= 64)
     return launch_attn_t<T, D, W, true, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
-                                              ws, approx, order, st);
+                                              ws, approx, order, stages, st);
   // at d = 64 the values stay in LDS up to 256 parents; beyond, LDS-resident
   // values would leave one workgroup per CU, with nothing to cover the
   // staged parent passes' barriers (measured at 512 flat codewords: 211 us
@@ -1383,32 +1384,32 @@ static hipError_t launch_attn_v(const void* Q, const void* cb, const float* vsum
   if constexpr (D == 64) {
     if (M0 <= 256)
       return launch_attn_t<T, D, W, false, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp,
-                                                 importance, ws, approx, order, st);
+                                                 importance, ws, approx, order, stages, st);
   }
   return launch_attn_t<T, D, W, false, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
-                                              ws, approx, order, st);
+                                              ws, approx, order, stages, st);
 }
 
 template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, const int* order, hipStream_t st) {
+                                void* ws, bool approx, const int* order, int stages, hipStream_t st) {
   if (C <= 8)
     return launch_attn_v<T, D, 8>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx,
-                                  order, st);
+                                  order, stages, st);
   return launch_attn_v<T, D, 16>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx,
-                                 order, st);
+                                 order, stages, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, bool approx, const int* order, hipStream_t st) {
+                            float* importance, void* ws, bool approx, const int* order, int stages, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
-    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
+    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
   }
-  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
-  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, st);
+  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
+  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
 }
 
 }  // namespace avq

@@ -30,9 +30,12 @@ hipError_t launch_zero(float* vsum, int64_t nv, float* ksum, int64_t nk, int* co
 hipError_t launch_assign(int dtype, const void* K, const void* V, const void* cb, int BH, int H, int N, int d, int M0,
                          int C, float* vsum, int* counts, int* assign, float* ksum, hipStream_t st);
 size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH);
+// stages of launch_attention: the value fragments of the workspace, the attention kernel
+constexpr int kAttnPrep = 1;
+constexpr int kAttnKernel = 2;
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, bool approx, const int* order, hipStream_t st);
+                            float* importance, void* ws, bool approx, const int* order, int stages, hipStream_t st);
 hipError_t launch_codebook_update(const float* ksum, const int* counts, int B, int H, int d, int M0, int C,
                                   float decay, float* S, float* Nm, float* cb, hipStream_t st);
 

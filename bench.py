@@ -1,22 +1,28 @@
 #!/usr/bin/env python3
 """Throughput of the AVQ-Attention forward pass on one MI355X.
 
-One step = one pass of the whole hot path over one batch: call 1
-(avq_assign_aggregate: zero fill + two-level assignment + value sums and
-counts) then call 2 (avq_attention_fwd: per-head fp16 value fragments, then
-parent attention, importance, top-P, child correction, output), both through
-the C interface, on synthetic inputs already resident in HBM.  Three input
-sets are rotated (larger than the 256 MB Infinity Cache together) so that
-every step streams from HBM.
+One step = one pass of the whole hot path over one batch, through the C
+interface, on synthetic inputs already resident in HBM:
+  avq_assign_aggregate        zero fill + two-level assignment + value sums
+                              and counts (Sec. 4.2, Alg. 1, Eq. 3)
+  avq_attention_prepare       the value sums as fp16 operand fragments
+  avq_attention_fwd_prepared  the attention kernel: parent attention,
+                              importance, top-P, child correction, output
+                              (Sec. 4.3, Alg. 2, Eq. 6-9)
+The three calls are issued with their arguments marshalled once (ctypes
+argument tuples built before the timed loop), so the timed loop adds no
+Python-side checking between launches.  Three input sets are rotated (larger
+than the 256 MB Infinity Cache together) so that every step streams from HBM.
 
 Prints one JSON line:
   value            tokens per second of the whole pass, in millions (B*N / step time)
-  roofline         the dominant call's algorithmic bytes per call over its
-                   average duration (HIP events on the launch stream around the
-                   call, inside the timed region) against MI355X's 8 TB/s HBM
-                   peak; traffic = counter-measured HBM bytes per call
-  kernels          the same figures for both calls (and the kernels each
-                   launches), with MFMA fractions
+  roofline         the dominant unit (the attention kernel): its algorithmic
+                   bytes per launch over its average duration (HIP events on
+                   the launch stream around the call, inside the timed
+                   region) against MI355X's 8 TB/s HBM peak, and its
+                   algorithmic MFMA flops against the 2.5 PFLOP/s dense bf16
+                   peak; traffic = counter-measured HBM bytes per launch
+  units            the same figures for every unit of the step
   cpu_baseline     the CPU oracle on the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload grid128]
@@ -39,15 +45,16 @@ METRIC = "AVQ fwd Mtokens/s at N=16384,H=16,d=64,M0=64,C=8,P=16; % HBM/MFMA roof
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MFMA_FP32_PEAK_TFLOPS = 157.3
+_ATTN_SRC = ["adaptive_vector_quantized_amd/csrc/attention.hip", "adaptive_vector_quantized_amd/csrc/avq_device.h",
+             "adaptive_vector_quantized_amd/csrc/avq_launch.h"]
 # each timed unit is one C call; the kernels it launches, and their sources
 CALLS = {
     "avq_assign_aggregate": ("zero_kernel + assign_aggregate_kernel",
                              ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
                               "adaptive_vector_quantized_amd/csrc/avq_device.h"]),
-    "avq_attention_fwd": ("attention_prep_kernel + attention_kernel",
-                          ["adaptive_vector_quantized_amd/csrc/attention.hip",
-                           "adaptive_vector_quantized_amd/csrc/avq_device.h",
-                           "adaptive_vector_quantized_amd/csrc/avq_launch.h"]),
+    "avq_attention_prepare": ("attention_prep_kernel", _ATTN_SRC),
+    "avq_attention_fwd_prepared": ("attention_kernel (or attention_pipe_kernel)", _ATTN_SRC),
+    "avq_attention_fwd": ("attention_prep_kernel + attention_kernel", _ATTN_SRC),
 }
 
 
@@ -60,22 +67,33 @@ def source_hash(call: str) -> str:
 
 
 def algorithmic(cfg, P):
-    """Bytes each kernel must move and flops it must do, per launch.
+    """Bytes each unit must move and flops it must do, per launch.
 
-    Kernel 1: read K and V once, the head codebooks once, write the value sums
-    and counts once; flops 2 d (M0 + C) per key (parent and child distances).
-    Kernel 2: read Q once, write Y (float32) once, read codebooks, value sums
-    and counts once; MFMA flops 4 d (M0 + P C) per query (logits and weighted
-    value sums over the M0 + P C codewords a tile uses)."""
+    avq_assign_aggregate: read K and V once, the head codebooks once, write
+    the value sums and counts once; flops 2 d (M0 + C) per key (parent and
+    child distances).
+    avq_attention_prepare: read the value sums (float) once, write them once
+    as operands (fp16 for bf16 inputs, float for fp32 inputs).
+    avq_attention_fwd_prepared (the attention kernel): read Q once, write Y
+    (float32) once, read the codebooks, the counts and the value operands
+    once; MFMA flops 4 d (M0 + P C) per query (logits and weighted value sums
+    over the M0 + P C codewords a tile uses).
+    avq_attention_fwd (both, as one call): Q, Y, codebooks, float value sums
+    and counts once, the same flops."""
     es = 2 if cfg.dtype == "bf16" else 4
     BH, N, d, M0, C, Mt = cfg.BH, cfg.N, cfg.d, cfg.M0, cfg.C, cfg.Mt
     cb = cfg.H * Mt * d * es
     aggr = BH * Mt * (d * 4 + 4)
+    operands = BH * Mt * d * es
     k1_bytes = 2 * BH * N * d * es + cb + aggr
     k2_bytes = BH * N * d * es + BH * N * d * 4 + cb + aggr
+    kern_bytes = BH * N * d * es + BH * N * d * 4 + cb + BH * Mt * 4 + operands
     k1_flops = 2.0 * d * (M0 + C) * BH * N
     k2_flops = 4.0 * d * (M0 + P * C) * BH * N
-    return {"avq_assign_aggregate": (k1_bytes, k1_flops), "avq_attention_fwd": (k2_bytes, k2_flops)}
+    return {"avq_assign_aggregate": (k1_bytes, k1_flops),
+            "avq_attention_prepare": (BH * Mt * d * 4 + operands, 0.0),
+            "avq_attention_fwd_prepared": (kern_bytes, k2_flops),
+            "avq_attention_fwd": (k2_bytes, k2_flops)}
 
 
 def load_traffic(call: str, workload: str):
@@ -142,6 +160,85 @@ def cpu_baseline(cfg, P, runs: int = 3):
     }
 
 
+class Step:
+    """The C calls of one pass over one input set (a dict of device tensors:
+    K, V, Q, cb, vsum, counts, Y, ws), with their ctypes arguments built once,
+    after one checked call through the binding.  With approx or qorder the
+    attention is one call of avq_attention_fwd_approx / _ordered (preparation
+    included); otherwise it is avq_attention_prepare then
+    avq_attention_fwd_prepared."""
+
+    def __init__(self, cfg, P, s, stream, approx=False, qorder=None, block_q=None):
+        import ctypes
+        import torch
+        from adaptive_vector_quantized_amd import _lib
+        L = _lib.lib()
+        bq = block_q or cfg.block_q
+        dt = _lib.AVQ_BF16 if s["Q"].dtype == torch.bfloat16 else _lib.AVQ_F32
+        ptr = _lib._ptr
+        st = ctypes.c_void_p(stream.cuda_stream)
+        shp = (cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C, dt)
+        # one checked call of each through the binding (shapes, dtypes, devices)
+        _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
+        self.calls = [("avq_assign_aggregate", L.avq_assign_aggregate,
+                       (ptr(s["K"]), ptr(s["V"]), ptr(s["cb"])) + shp + (ptr(s["vsum"]), ptr(s["counts"]), None, st))]
+        wsb = s["ws"].numel()
+        tail = (P, bq, float(cfg.scale))
+        if approx or qorder is not None:
+            _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, bq, cfg.scale, Y=s["Y"],
+                               workspace=s["ws"], approx_denominator=approx, query_order=qorder)
+            if qorder is not None:
+                args = (ptr(s["Q"]), ptr(s["cb"]), ptr(s["vsum"]), ptr(s["counts"])) + shp + tail + (
+                    ptr(qorder), 1 if approx else 0, ptr(s["Y"]), None, None, ptr(s["ws"]), wsb, st)
+                self.calls.append(("avq_attention_fwd", L.avq_attention_fwd_ordered, args))
+            else:
+                args = (ptr(s["Q"]), ptr(s["cb"]), ptr(s["vsum"]), ptr(s["counts"])) + shp + tail + (
+                    ptr(s["Y"]), None, None, ptr(s["ws"]), wsb, st)
+                self.calls.append(("avq_attention_fwd", L.avq_attention_fwd_approx, args))
+        else:
+            _lib.attention_prepare(s["vsum"], cfg.C, s["Q"].dtype, workspace=s["ws"])
+            _lib.attention_fwd_prepared(s["Q"], s["cb"], s["counts"], s["ws"], cfg.C, P, bq, cfg.scale, Y=s["Y"])
+            self.calls.append(("avq_attention_prepare", L.avq_attention_prepare,
+                               (ptr(s["vsum"]), cfg.B, cfg.H, cfg.d, cfg.M0, cfg.C, dt, ptr(s["ws"]), wsb, st)))
+            self.calls.append(("avq_attention_fwd_prepared", L.avq_attention_fwd_prepared,
+                               (ptr(s["Q"]), ptr(s["cb"]), ptr(s["counts"])) + shp + tail + (
+                                   ptr(s["Y"]), None, None, ptr(s["ws"]), wsb, st)))
+        self.names = [c[0] for c in self.calls]
+
+    def run(self, events=None):
+        """Issue the pass; events (one more than the calls) are recorded
+        before the first call and after each."""
+        if events is not None:
+            events[0].record()
+        for i, (name, fn, args) in enumerate(self.calls):
+            rc = fn(*args)
+            if rc != 0:
+                raise RuntimeError(f"{name} returned {rc}")
+            if events is not None:
+                events[i + 1].record()
+
+
+def timed_steps(steps_by_set, n_steps, warmup):
+    """Warm up, then time n_steps passes rotating over the input sets: wall
+    time, and per-unit durations (seconds, one row per step) from events on
+    the launch stream."""
+    import torch
+    for i in range(warmup):
+        steps_by_set[i % len(steps_by_set)].run()
+    torch.cuda.synchronize()
+    n_units = len(steps_by_set[0].calls)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_units + 1)] for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        steps_by_set[i % len(steps_by_set)].run(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(n_units)] for e in ev]) * 1e-3
+    span = ev[0][0].elapsed_time(ev[-1][-1]) * 1e-3
+    return wall, per, span
+
+
 def complexity(args):
     """Both calls over N in {4096, 16384, 65536} (B = 2, H = 16, d = 64, bf16) for flat
     codebooks of M in {64, 128, 256, 512} (P = 0) and a hierarchical one (M0 = 64, C = 8,
@@ -150,7 +247,8 @@ def complexity(args):
     attends to (M, or M0 + P C).  Queries and values are seeded N(0, 1) draws on the device; a
     codebook from the generator; keys are a codeword plus noise, one codeword per run of 64
     consecutive tokens (the locality of the image workloads' 8x8 patches), or per token with
-    --complexity-order random.  One JSON line with every point and the log-log slopes."""
+    --complexity-order random.  The attention time is avq_attention_prepare plus
+    avq_attention_fwd_prepared.  One JSON line with every point and the log-log slopes."""
     import torch
     from adaptive_vector_quantized_amd import _lib, gen
     dev = torch.device("cuda:0")
@@ -168,35 +266,27 @@ def complexity(args):
         Q, K, V = (torch.randn((B, H, N, d), generator=g, device=dev).to(torch.bfloat16).contiguous()
                    for _ in range(3))
         for kind, M0, C, P in shapes:
+            cfg = gen.Config(f"complexity-{kind}", B=B, H=H, N=N, d=d, M0=M0, C=C, P=P, block_q=128, dtype="bf16",
+                             grid=None, parents="uniform", seed=3000 + M0 + C)
             cb = torch.from_numpy(gen.make_codebook(3000 + M0 + C, H, M0, C, d)).to(torch.bfloat16).contiguous().to(dev)
             Mt = M0 * (1 + C)
-            vsum = torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev)
-            counts = torch.empty((B, H, Mt), dtype=torch.int32, device=dev)
-            Y = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
-            ws = torch.empty(_lib.workspace_size(B, H, d, M0, C, torch.bfloat16), dtype=torch.uint8, device=dev)
             run = 1 if args.complexity_order == "random" else 64
             idx = torch.randint(0, Mt, (B, H, N // run), generator=g, device=dev).repeat_interleave(run, dim=2)
             Kc = (cb.float()[torch.arange(H, device=dev)[None, :, None], idx] + 0.1 * K.float()).to(torch.bfloat16)
-            Kc = Kc.contiguous()
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-            for i in range(warm + steps):
-                e = ev[i - warm] if i >= warm else None
-                if e:
-                    e[0].record(stream)
-                _lib.assign_aggregate(Kc, V, cb, C, vsum=vsum, counts=counts)
-                if e:
-                    e[1].record(stream)
-                _lib.attention_fwd(Q, cb, vsum, counts, C, P, 128, 1.0 / d ** 0.5, Y=Y, workspace=ws)
-                if e:
-                    e[2].record(stream)
-            torch.cuda.synchronize()
-            k1 = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
-            k2 = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+            s = {"K": Kc.contiguous(), "V": V, "Q": Q, "cb": cb,
+                 "vsum": torch.empty((B, H, Mt, d), dtype=torch.float32, device=dev),
+                 "counts": torch.empty((B, H, Mt), dtype=torch.int32, device=dev),
+                 "Y": torch.empty((B, H, N, d), dtype=torch.float32, device=dev),
+                 "ws": torch.empty(_lib.workspace_size(B, H, d, M0, C, torch.bfloat16), dtype=torch.uint8,
+                                   device=dev)}
+            _, per, _ = timed_steps([Step(cfg, P, s, stream)], steps, warm)
+            k1 = float(np.median(per[:, 0])) * 1e6
+            k2 = float(np.median(per[:, 1] + per[:, 2])) * 1e6
             rows.append({"N": N, "kind": kind, "M0": M0, "C": C, "P": P, "precompute_codes": M0 + C,
                          "attention_codes": M0 + P * C, "assign_aggregate_us": round(k1, 2),
                          "attention_fwd_us": round(k2, 2)})
             print(f"[bench] {rows[-1]}", file=sys.stderr, flush=True)
-            del cb, vsum, counts, Y, ws, Kc
+            del cb, s, Kc
         del Q, K, V
         torch.cuda.empty_cache()
 
@@ -204,8 +294,9 @@ def complexity(args):
         return float(np.polyfit(np.log(xs), np.log(ys), 1)[0])
     fits = {}
     for col, codes in (("assign_aggregate_us", "precompute_codes"), ("attention_fwd_us", "attention_codes")):
-        byN = [slope([r["N"] for r in rows if (r["kind"], r["M0"], r["P"]) == key], [r[col] for r in rows if (r["kind"], r["M0"], r["P"]) == key])
-               for key in {(r["kind"], r["M0"], r["P"]) for r in rows}]
+        keys = sorted({(r["kind"], r["M0"], r["P"]) for r in rows})
+        byN = [slope([r["N"] for r in rows if (r["kind"], r["M0"], r["P"]) == key],
+                     [r[col] for r in rows if (r["kind"], r["M0"], r["P"]) == key]) for key in keys]
         vq = [r for r in rows if r["kind"] == "vq" and r["N"] == 65536]
         fits[col] = {"slope_in_N": [round(x, 3) for x in sorted(byN)],
                      "slope_in_codes_flat_N65536": round(slope([r[codes] for r in vq], [r[col] for r in vq]), 3)}
@@ -295,37 +386,8 @@ def main():
             raise SystemExit("--query-order gilbert needs a workload on a token grid")
         qorder = torch.from_numpy(gilbert.query_order(cfg.grid, cfg.grid)).to(dev)
 
-    def timed(P, steps, warmup):
-        """Warm up, then time `steps` whole passes at refinement budget P: wall
-        time, and per-call durations from events on the launch stream."""
-        def step(s):
-            _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
-            _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
-                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator,
-                               query_order=qorder)
-
-        for i in range(warmup):
-            step(sets[i % len(sets)])
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            s = sets[i % len(sets)]
-            e = ev[i]
-            e[0].record(stream)
-            _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
-            e[1].record(stream)
-            _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, cfg.block_q, cfg.scale,
-                               Y=s["Y"], workspace=s["ws"], approx_denominator=args.approx_denominator,
-                               query_order=qorder)
-            e[2].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        k1 = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3  # seconds
-        k2 = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-        span = ev[0][0].elapsed_time(ev[-1][2]) * 1e-3
-        return wall, k1, k2, span
+    def steps_at(Ps):
+        return [Step(cfg, Ps, s_, stream, approx=args.approx_denominator, qorder=qorder) for s_ in sets]
 
     if args.codebook_update != "none":
         # forward pass + codebook update: one line with the step rate and per-call times
@@ -385,11 +447,13 @@ def main():
         # one line: the whole pass at every refinement budget of the workload
         rows = []
         for Ps in (cfg.sweep_P or (P,)):
-            wall, k1, k2, _ = timed(Ps, args.steps, args.warmup)
-            rows.append({"P": Ps, "value": round(cfg.B * cfg.N / (wall / args.steps) / 1e6, 3),
-                         "ms_per_step": round(wall / args.steps * 1e3, 5),
-                         "avq_assign_aggregate_us": round(float(k1.mean()) * 1e6, 2),
-                         "avq_attention_fwd_us": round(float(k2.mean()) * 1e6, 2)})
+            st_ = steps_at(Ps)
+            wall, per, _ = timed_steps(st_, args.steps, args.warmup)
+            row = {"P": Ps, "value": round(cfg.B * cfg.N / (wall / args.steps) / 1e6, 3),
+                   "ms_per_step": round(wall / args.steps * 1e3, 5)}
+            for j, n in enumerate(st_[0].names):
+                row[f"{n}_us"] = round(float(per[:, j].mean()) * 1e6, 2)
+            rows.append(row)
             print(f"[bench] P={Ps}: {rows[-1]}", file=sys.stderr, flush=True)
         print(json.dumps({"metric": "AVQ fwd Mtokens/s versus the refinement budget P", "unit": "Mtokens/s",
                           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
@@ -399,7 +463,8 @@ def main():
                           "sweep": rows}), flush=True)
         return
 
-    wall, k1, k2, gpu_span = timed(P, args.steps, args.warmup)
+    st_ = steps_at(P)
+    wall, per, gpu_span = timed_steps(st_, args.steps, args.warmup)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -413,21 +478,21 @@ def main():
     value = tokens / (wall / args.steps) / 1e6
     alg = algorithmic(cfg, P)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
-    kernels = {}
-    for name, t in (("avq_assign_aggregate", k1), ("avq_attention_fwd", k2)):
+    units = {}
+    for j, name in enumerate(st_[0].names):
         b, f = alg[name]
+        t = per[:, j]
         avg = float(t.mean())
-        kernels[name] = {
+        units[name] = {
             "launches": CALLS[name][0],
             "avg_us": avg * 1e6, "median_us": float(np.median(t)) * 1e6,
             "algorithmic_bytes": b, "algorithmic_flops": f,
             "GBps": b / avg / 1e9, "hbm_frac": b / avg / 1e9 / HBM_PEAK_GBS,
             "TFLOPs": f / avg / 1e12, "mfma_frac": f / avg / 1e12 / mfma_peak,
         }
-    dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    kd = kernels[dom]
-    # counters taken on the exact call in row-major order
-    traffic = None if (args.approx_denominator or qorder is not None) else load_traffic(dom, cfg.name)
+    dom = max(units, key=lambda k: units[k]["avg_us"])
+    kd = units[dom]
+    traffic = load_traffic(dom, cfg.name) if qorder is None else None
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -450,12 +515,16 @@ def main():
             "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "parallelism": "single GPU",
         },
         "roofline": {
-            "call": dom, "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "call": dom, "kernel": CALLS[dom][0],
+            "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kd["hbm_frac"], 4), "traffic": traffic,
+            "mfma": {"achieved": round(kd["TFLOPs"], 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                     "frac": round(kd["mfma_frac"], 4)},
         },
-        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kernels.items()},
+        "units": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                  for k, v in units.items()},
         "gpu_span_ms_per_step": round(gpu_span / max(1, args.steps - 1) * 1e3, 5),
+        "unit_sum_ms_per_step": round(float(per.sum(axis=1).mean()) * 1e3, 5),
         "Mhead_tokens_per_s": round(cfg.B * cfg.H * cfg.N / (wall / args.steps) / 1e6, 3),
     }
     if not args.no_cpu_baseline:

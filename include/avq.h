@@ -118,7 +118,9 @@ int avq_assign_aggregate_kv(const void* K, const void* V, const void* codebook, 
  * Bytes of device workspace avq_attention_fwd needs for these sizes (0 if the
  * sizes are invalid).  The workspace holds the value sums of every codeword
  * converted to the operand format of the weighted-value products; it is
- * written and read by one call and carries nothing between calls.
+ * written and read by one call of avq_attention_fwd and carries nothing
+ * between such calls.  avq_attention_prepare and avq_attention_fwd_prepared
+ * split that call in two around the same workspace.
  */
 size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C,
                                     int dtype);
@@ -222,6 +224,39 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                               const int32_t* query_order, int approx_denominator,
                               float* Y, int32_t* topp, float* importance,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of avq_attention_fwd, for callers that attend several query
+ * batches to one set of aggregates (Eq. 3: the value sums and counts depend
+ * on the keys only), and to time the attention kernel on its own.
+ *
+ * avq_attention_prepare converts the value sums (Eq. 3, from
+ * avq_assign_aggregate) into the operands of the weighted-value products
+ * (Eq. 6 and 9) and writes them to the workspace: one launch, reading vsum
+ * and writing the workspace.  Q, codebook, counts and P play no part, and N
+ * is not needed.
+ *
+ * avq_attention_fwd_prepared is then the rest of avq_attention_fwd for one
+ * query batch: the attention kernel alone, reading the operands from a
+ * workspace that avq_attention_prepare filled with the same B, H, d, M0, C
+ * and dtype from the value sums that go with these counts, unchanged since;
+ * it does not write the
+ * workspace, so any number of such calls may follow one preparation, also
+ * concurrently on different streams once the preparation has completed.
+ * Given those, its outputs are bit for bit those of avq_attention_fwd on the
+ * same arguments.  A workspace not prepared so gives unspecified (but
+ * memory-safe) outputs.
+ *
+ * Arguments, layouts and errors are those of avq_attention_fwd; prepare
+ * checks only what it uses (vsum, the workspace and the sizes).
+ */
+int avq_attention_prepare(const float* vsum, int B, int H, int d, int M0, int C, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int avq_attention_fwd_prepared(const void* Q, const void* codebook, const int32_t* counts,
+                               int B, int H, int N, int d, int M0, int C, int dtype,
+                               int P, int block_q, float scale, float* Y, int32_t* topp,
+                               float* importance, const void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * avq_attention_fwd without a workspace argument, for callers that cannot

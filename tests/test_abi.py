@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
     assert set(names) == {"avq_assign_aggregate", "avq_assign_aggregate_kv", "avq_attention_fwd", "avq_attention_fwd_approx",
-                          "avq_attention_fwd_ordered", "avq_attention_fwd_noalloc", "avq_attention_workspace_size",
+                          "avq_attention_fwd_ordered", "avq_attention_fwd_noalloc", "avq_attention_prepare",
+                          "avq_attention_fwd_prepared", "avq_attention_workspace_size",
                           "avq_codebook_update", "avq_status_string", "avq_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -64,6 +65,10 @@ def _call_attn(L, fn="avq_attention_fwd", **kw):
         return L.avq_attention_fwd_noalloc(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"],
                                            a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"],
                                            a["topp"], a["imp"], None)
+    if fn == "avq_attention_fwd_prepared":
+        return L.avq_attention_fwd_prepared(a["Q"], a["cb"], a["counts"], a["B"], a["H"], a["N"], a["d"], a["M0"],
+                                            a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"],
+                                            a["imp"], a["ws"], a["wsb"], None)
     if fn == "avq_attention_fwd_ordered":
         return L.avq_attention_fwd_ordered(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"],
                                            a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["order"],
@@ -102,7 +107,7 @@ def test_assign_validation(L, kv):
 
 
 @pytest.mark.parametrize("fn", ["avq_attention_fwd", "avq_attention_fwd_approx", "avq_attention_fwd_ordered",
-                                "avq_attention_fwd_noalloc"])
+                                "avq_attention_fwd_noalloc", "avq_attention_fwd_prepared"])
 def test_attention_validation(L, fn):
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 8)
@@ -139,6 +144,32 @@ def test_attention_validation(L, fn):
     assert L.avq_attention_workspace_size(1, 1, 96, 4, 2, 1) == 0   # invalid sizes
     assert _attn(L, N=0) == 0         # no queries: nothing to do
     assert _attn(L, B=0, Q=None) == 0
+
+
+def test_prepare_validation(L):
+    """avq_attention_prepare checks the sizes, the value sums and the workspace
+    (it reads nothing else)."""
+    _, p = _buf()
+    mis = ctypes.c_void_p(p.value + 8)
+
+    def _prep(**kw):
+        a = dict(vsum=p, B=1, H=1, d=64, M0=4, C=2, dtype=1, ws=p, wsb=1 << 30)
+        a.update(kw)
+        return L.avq_attention_prepare(a["vsum"], a["B"], a["H"], a["d"], a["M0"], a["C"], a["dtype"], a["ws"],
+                                       a["wsb"], None)
+    assert _prep(dtype=2) == -3
+    assert _prep(B=-1) == -2
+    assert _prep(M0=0) == -2
+    assert _prep(C=-1) == -2
+    assert _prep(d=32) == -5
+    assert _prep(M0=513) == -5
+    assert _prep(vsum=None) == -1
+    assert _prep(ws=None) == -1
+    assert _prep(vsum=mis) == -4
+    assert _prep(ws=mis) == -4
+    need = L.avq_attention_workspace_size(1, 1, 64, 4, 2, 1)
+    assert _prep(wsb=need - 1) == -7
+    assert _prep(B=0, vsum=None) == 0   # no (batch, head): nothing to do
 
 
 def test_ordered_validation(L):

@@ -31,6 +31,14 @@ def test_algorithmic_counts_grid128():
     assert round(k1f / 1e9, 2) == 4.83 and round(k2f / 1e9, 1) == 25.8
     # per query: 49152 MFMA flops at this workload (Tab. 1's O((M0 + P C) d))
     assert k2f / (BH * N) == 49152
+    # the call split in two: the preparation moves the value sums (float in,
+    # fp16 operands out); the attention kernel reads the operands instead
+    pb, pf = alg["avq_attention_prepare"]
+    kb, kf = alg["avq_attention_fwd_prepared"]
+    assert pb == BH * Mt * d * (4 + 2) and pf == 0
+    assert kb == BH * N * d * (2 + 4) + cb + BH * Mt * 4 + BH * Mt * d * 2
+    assert kf == k2f
+    assert round(kb / 1e6, 1) == 204.9
 
 
 def test_refinement_budget_enters_kernel2_only():
@@ -38,6 +46,8 @@ def test_refinement_budget_enters_kernel2_only():
     a0, a64 = bench.algorithmic(cfg, 0), bench.algorithmic(cfg, 64)
     assert a0["avq_assign_aggregate"] == a64["avq_assign_aggregate"]
     assert a64["avq_attention_fwd"][1] - a0["avq_attention_fwd"][1] == 4 * cfg.d * 64 * cfg.C * cfg.BH * cfg.N
+    assert a0["avq_attention_prepare"] == a64["avq_attention_prepare"]
+    assert a64["avq_attention_fwd_prepared"][1] == a64["avq_attention_fwd"][1]
 
 
 def test_multi_gpu_request_exits():
