@@ -157,28 +157,76 @@ __device__ __forceinline__ void select_top(const uint32_t (&u)[NG], int M0, int 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kYRow = 36;  // floats per staged output row (32 dims + 4 to spread LDS banks)
 
-size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) {
+// Workspace: [BH] value scales | [BH] value operand fragments | [BH][slices]
+// partial maxima of |vsum| (one per slice of kMaxSlice4 float4 of a head's
+// value sums).
+constexpr int kMaxThreads = 256;               // threads of the partial-maximum kernel
+constexpr int kMaxPer = 4;                     // float4 loads per thread
+constexpr int kMaxSlice4 = kMaxThreads * kMaxPer;
+struct AttnWs {
+  size_t sig_bytes, per_bh, pmax_off, total;
+  int slices;
+};
+static AttnWs attn_ws(int dtype, int d, int M0, int C, int BH) {
+  AttnWs w;
   const size_t pes = dtype == 0 ? 4 : 2;
   const size_t M0p = attn_parent_rows(M0);
   const size_t W = C == 0 ? 0 : C <= 8 ? 8 : 16;  // a flat codebook has no child fragments
-  const size_t per = align256((M0p * d + (size_t)M0 * W * d) * pes);
-  return align256((size_t)BH * 4) + (size_t)BH * per;
+  const size_t n4 = (size_t)M0 * (1 + C) * d / 4;
+  w.sig_bytes = align256((size_t)BH * 4);
+  w.per_bh = align256((M0p * d + (size_t)M0 * W * d) * pes);
+  w.slices = (int)((n4 + kMaxSlice4 - 1) / kMaxSlice4);
+  w.pmax_off = w.sig_bytes + (size_t)BH * w.per_bh;
+  w.total = w.pmax_off + align256((size_t)BH * w.slices * 4);
+  return w;
 }
 
-// Prep: one round of loads per thread.  Every block of a (batch, head) first
-// issues the gathers of its own fragments (at most kPrepFrag per thread) and
-// its share of the head's maximum, reduces the maximum, then scales, packs and
-// stores.  The blocks of a head each form the maximum themselves (the head's
-// value sums are a few hundred KB, read from L2), so no second launch and no
-// inter-block wait is needed.
+size_t attention_workspace_bytes(int dtype, int d, int M0, int C, int BH) { return attn_ws(dtype, d, M0, C, BH).total; }
+
+// Prep: attention_prep_kernel, one round of loads per thread; every block of
+// a (batch, head) issues the gathers of its own fragments (at most kPrepFrag
+// per thread), forms the head's maximum |value sum|, then scales, packs and
+// stores.  For a small head every block forms the maximum itself from the
+// head's value sums (a few hundred KB, read from L2): one launch, no wait
+// between blocks.  For a large head, where those repeated reads would cost
+// more than a launch, attention_absmax_kernel first takes the maximum of each
+// slice of kMaxSlice4 float4 (every value sum read once) and the blocks then
+// combine the slices' maxima.
 constexpr int kPrepThreads = 512;
 constexpr int kPrepFrag = 2;   // fragments per thread
 constexpr int kPrepMax = 18;   // f32x4 loads in flight per thread for the maximum
+constexpr size_t kPrepRepeatBytes = 8u << 20;  // repeated reads of one head's sums beyond which the maximum is split
+
+__global__ __launch_bounds__(kMaxThreads) void attention_absmax_kernel(const float* __restrict__ vsum, int n4,
+                                                                       int slices, float* __restrict__ pmax) {
+  __shared__ float red[kMaxThreads / 64];
+  const int bh = blockIdx.x / slices, sl = blockIdx.x % slices;
+  const f32x4* v = (const f32x4*)vsum + (int64_t)bh * n4;
+  const int tid = threadIdx.x;
+  f32x4 x[kMaxPer];
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int i = sl * kMaxSlice4 + u * kMaxThreads + tid;
+    x[u] = i < n4 ? v[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float mx = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) mx = fmaxf(mx, absmax4(x[u]));
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < kMaxThreads / 64; ++w) mx = fmaxf(mx, red[w]);
+    pmax[blockIdx.x] = mx;
+  }
+}
 
 template <class T, int D, int W>
 __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const float* __restrict__ vsum, int BH, int M0,
                                                                       int C, int parts, unsigned char* __restrict__ ws,
-                                                                      size_t sig_bytes, size_t per_bh) {
+                                                                      size_t sig_bytes, size_t per_bh,
+                                                                      const float* __restrict__ pmax, int slices) {
   using pvfrag_t = typename T::pvfrag_t;
   constexpr int E = T::E;
   constexpr int KV = 16 / E;
@@ -231,17 +279,21 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   }
   float sig = 1.0f;
   if constexpr (T::kScaleValues) {
-    const int n4 = Mt * (D / 4);
     float mx = 0.0f;
-    for (int i0 = tid; i0 < n4; i0 += kPrepThreads * kPrepMax) {
-      f32x4 v[kPrepMax];
+    if (pmax != nullptr) {
+      for (int i = tid; i < slices; i += kPrepThreads) mx = fmaxf(mx, pmax[(int64_t)bh * slices + i]);
+    } else {
+      const int n4 = Mt * (D / 4);
+      for (int i0 = tid; i0 < n4; i0 += kPrepThreads * kPrepMax) {
+        f32x4 v[kPrepMax];
 #pragma unroll
-      for (int u = 0; u < kPrepMax; ++u) {
-        const int i = i0 + u * kPrepThreads;
-        v[u] = ((const f32x4*)vs)[i < n4 ? i : 0];
+        for (int u = 0; u < kPrepMax; ++u) {
+          const int i = i0 + u * kPrepThreads;
+          v[u] = ((const f32x4*)vs)[i < n4 ? i : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kPrepMax; ++u) mx = fmaxf(mx, absmax4(v[u]));
       }
-#pragma unroll
-      for (int u = 0; u < kPrepMax; ++u) mx = fmaxf(mx, absmax4(v[u]));
     }
     mx = wave_max(mx);
     if (lane == 0) red[wave] = mx;
@@ -1329,16 +1381,25 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
                                 void* ws, bool approx, const int* order, int stages, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
-  const size_t sig_bytes = align256((size_t)BH * 4);
-  const size_t per_bh = (attention_workspace_bytes(dtype, D, M0, C, BH) - sig_bytes) / (BH > 0 ? BH : 1);
+  const AttnWs wl = attn_ws(dtype, D, M0, C, BH);
+  const size_t sig_bytes = wl.sig_bytes, per_bh = wl.per_bh;
   if (stages & kAttnPrep) {
     constexpr int E = T::E, KV = 16 / E;
     const int M0p = attn_parent_rows(M0);
     const int nF = (M0p / 32) * KV * 2 * D + (C > 0 ? M0 * (W / E) * D : 0);
     const int per_part = kPrepThreads * kPrepFrag;
     const int parts = std::max(8, (nF + per_part - 1) / per_part);
+    const size_t head_bytes = (size_t)M0 * (1 + C) * D * 4;
+    float* pmax = nullptr;
+    if (T::kScaleValues && (size_t)parts * head_bytes > kPrepRepeatBytes) {
+      pmax = (float*)((unsigned char*)ws + wl.pmax_off);
+      hipLaunchKernelGGL(attention_absmax_kernel, dim3(BH * wl.slices), dim3(kMaxThreads), 0, st, vsum,
+                         M0 * (1 + C) * (D / 4), wl.slices, pmax);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, BH, M0,
-                       C, parts, (unsigned char*)ws, sig_bytes, per_bh);
+                       C, parts, (unsigned char*)ws, sig_bytes, per_bh, (const float*)pmax, wl.slices);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
