@@ -546,27 +546,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int pt = 0; pt < nPT; ++pt) {
       const int j0 = pt * 64;
       if constexpr (!parents_lds) wait_pass();
+      // empty parents and padding rows (count 0) get logit -inf: their bias
+      // enters as the initial value of the accumulator (zero when every
+      // parent of the pass holds keys)
+      const bool pass_masked = !all_parents || j0 + 64 > M0;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int bb = parents_lds ? pt * 2 + b : b;
         lg[b] = zero16();
-#pragma unroll
-        for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
-      }
-      if constexpr (!parents_lds)
-        release_pass(pt + 1 < nPT ? pt + 1 : (second_pass || tile + 1 < tile1) ? 0 : -1);
-      if (!all_parents || j0 + 64 > M0) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        if (pass_masked) {
           const f32x4* bp = (const f32x4*)(sBp + j0 + b * 32 + 8 * hh);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) lg[b][q * 4 + u] += b4[u];
+            for (int u = 0; u < 4; ++u) lg[b][q * 4 + u] = b4[u];
           }
         }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) lg[b] = T::mma_in(sPC[(bb * KS + s) * 64 + lane], qf[s], lg[b]);
       }
+      if constexpr (!parents_lds)
+        release_pass(pt + 1 < nPT ? pt + 1 : (second_pass || tile + 1 < tile1) ? 0 : -1);
       float tm = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
@@ -642,19 +643,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           // second pass with the final stabiliser and denominator (exact Z of Eq. 7)
           wait_pass();
           f32x16 l2[2];
+          const bool pass_masked = !all_parents || j0 + 64 > M0;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             l2[b] = zero16();
+            if (pass_masked) {  // as in the first pass: empty parents and padding rows at -inf
+              const f32x4* bp = (const f32x4*)(sBp + j0 + b * 32 + 8 * hh);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) l2[b][q * 4 + u] = b4[u];
+              }
+            }
 #pragma unroll
             for (int s = 0; s < KS; ++s) l2[b] = T::mma_in(sPC[(b * KS + s) * 64 + lane], qf[s], l2[b]);
           }
           release_pass(pt + 1 < nPT ? pt + 1 : tile + 1 < tile1 ? 0 : -1);
+          // the stabiliser bounds every logit of a parent with keys (exp2 of
+          // at most the lazy margin) and the others are -inf: every term is
+          // finite, and exactly 0 for a parent without keys
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float n = sNp[j0 + b * 32 + col_of(r, hh)];
-              t[b * 16 + r] = n > 0.0f ? fast_exp2(fmaf(l2[b][r], sl2, -m)) * n * rz : 0.0f;
+              t[b * 16 + r] = fast_exp2(fmaf(l2[b][r], sl2, -m)) * (n * rz);
             }
         }
         // one pass: the count n_j of Eq. 7 is a factor of the whole sum over
