@@ -3,8 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <map>
 #include <mutex>
-#include <unordered_map>
 
 #include "../../include/avq.h"
 #include "avq_launch.h"
@@ -31,15 +31,22 @@ int from_hip(hipError_t e) { return e == hipSuccess ? AVQ_OK : AVQ_ERR_HIP; }
 
 namespace avq {
 
+// The largest dynamic LDS size already allowed for each (device, kernel):
+// the attribute is set once per device and kernel (and again only for a
+// larger size), under a lock, since calls may come from several host threads.
 hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
   if (bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   static std::mutex mu;
-  static std::unordered_map<const void*, size_t> done;
+  static std::map<std::pair<int, const void*>, size_t> done;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = done.find(kernel);
+  const auto key = std::make_pair(dev, kernel);
+  auto it = done.find(key);
   if (it != done.end() && it->second >= bytes) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) done[kernel] = bytes;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done[key] = bytes;
   return e;
 }
 

@@ -42,6 +42,7 @@
 // Children of a selected parent occupy W (8 or 16) consecutive accumulator
 // registers of one lane half, so S = 32 / W parents share a 32-row block.
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 
 #include "avq_device.h"
@@ -1104,18 +1105,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   };
 
   // Top-P of one tile (Alg. 2, the parent choice) from the importance
-  // partials of every wave; every wave forms its own copy of the selection.
+  // partials of every wave, formed by wave 0 alone into sSel; the other waves
+  // read it after the barrier that follows every call.
   auto top_p = [&](int tile) {
+    if (wave != 0) return;
     uint32_t u1[1];
     {
       const f32x4 p4 = *(const f32x4*)(sW + lane * 4);
       u1[0] = lane < M0 ? __float_as_uint((p4[0] + p4[1]) + (p4[2] + p4[3])) : 0u;
     }
-    if (importance && wave == 0 && lane < M0)
-      importance[((int64_t)bh * ntiles + tile) * M0 + lane] = __uint_as_float(u1[0]);
-    int* gout = (topp && wave == 0) ? topp + ((int64_t)bh * ntiles + tile) * P : nullptr;
-    select_top<1>(u1, M0, P, lane, sSel + wave * P, gout);
-    __builtin_amdgcn_wave_barrier();
+    if (importance && lane < M0) importance[((int64_t)bh * ntiles + tile) * M0 + lane] = __uint_as_float(u1[0]);
+    int* gout = topp ? topp + ((int64_t)bh * ntiles + tile) * P : nullptr;
+    select_top<1>(u1, M0, P, lane, sSel, gout);
   };
 
   // Copies of one stage of the selected parents' children into LDS (this
@@ -1124,7 +1125,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   const int r_row = r_of_row(ql), h_row = h_of_row(ql);
   const int s_row = 2 * (r_row / W) + h_row, c_row = r_row % W;
   auto stage_issue = [&](int st) {
-    const int* sel = sSel + wave * P;
+    const int* sel = sSel;
     const int b0 = st * SB;
     const int nb_st = min(SB, nCB - b0);
     for (int u = wave; u < nb_st * KS; u += nw) {
@@ -1374,14 +1375,17 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
 
 // Query tiles per workgroup: aim for about two resident workgroups per CU.
 int attention_tiles_per_wg(int BH, int N, int bq) {
-  // CU count of the device, read once (a function-local static is initialised
-  // once even under concurrent first calls)
-  static const int cus = [] {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      return v;
-    return 256;
-  }();
+  // CU count of the current device, read once per device (only the split of
+  // the work depends on it)
+  static std::atomic<int> cu_cache[64];
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    cus = cu_cache[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+      cu_cache[dev].store(cus, std::memory_order_relaxed);
+    }
+  }
   const int T = (N + bq - 1) / bq;
   const int target = 2 * cus;
   int per_bh = (target + BH - 1) / (BH > 0 ? BH : 1);

@@ -3,13 +3,39 @@ order the pages use so that a query tile of consecutive curve positions is a
 compact 2-D region of the image ("AVQ-Attention: Adaptive Vector-Quantized
 Attention", Sec. 4.3 and Fig. 3; the curve of ref. [34]).
 
-The curve is built by the usual recursive split of a rectangle given by an
-origin and two axis vectors (a: the major axis, b: the minor one): a long,
-thin rectangle is cut in two halves along a; otherwise it is cut into three
-parts (up along b, across along a, down along b back to the far corner).  Odd
-half-lengths are rounded so that the pieces keep even lengths where they can,
-which keeps consecutive cells adjacent for every grid whose sides are powers of
-two (and for most others).  Host-side utility: the attention call takes the
+The recursion in _walk follows, step for step, the "gilbert2d" reference
+implementation of the generalized Hilbert curve by Jakub Červený
+(github.com/jakubcerveny/gilbert), re-expressed as a Python generator: a
+rectangle given by an origin and two axis vectors (a: the major axis, b: the
+minor one) is cut in two halves along a when it is long and thin (2w > 3h),
+otherwise into three parts (up along b, across along a, down along b back to
+the far corner), odd half-lengths nudged so that the pieces keep even lengths
+where they can.  That implementation's licence notice:
+
+    BSD 2-Clause License
+    Copyright (c) 2018, Jakub Červený
+    All rights reserved.
+    Redistribution and use in source and binary forms, with or without
+    modification, are permitted provided that the following conditions are
+    met: 1. Redistributions of source code must retain the above copyright
+    notice, this list of conditions and the following disclaimer.
+    2. Redistributions in binary form must reproduce the above copyright
+    notice, this list of conditions and the following disclaimer in the
+    documentation and/or other materials provided with the distribution.
+    THIS SOFTWARE IS PROVIDED BY THE COPYRIGHT HOLDERS AND CONTRIBUTORS "AS
+    IS" AND ANY EXPRESS OR IMPLIED WARRANTIES, INCLUDING, BUT NOT LIMITED TO,
+    THE IMPLIED WARRANTIES OF MERCHANTABILITY AND FITNESS FOR A PARTICULAR
+    PURPOSE ARE DISCLAIMED. IN NO EVENT SHALL THE COPYRIGHT HOLDER OR
+    CONTRIBUTORS BE LIABLE FOR ANY DIRECT, INDIRECT, INCIDENTAL, SPECIAL,
+    EXEMPLARY, OR CONSEQUENTIAL DAMAGES (INCLUDING, BUT NOT LIMITED TO,
+    PROCUREMENT OF SUBSTITUTE GOODS OR SERVICES; LOSS OF USE, DATA, OR
+    PROFITS; OR BUSINESS INTERRUPTION) HOWEVER CAUSED AND ON ANY THEORY OF
+    LIABILITY, WHETHER IN CONTRACT, STRICT LIABILITY, OR TORT (INCLUDING
+    NEGLIGENCE OR OTHERWISE) ARISING IN ANY WAY OUT OF THE USE OF THIS
+    SOFTWARE, EVEN IF ADVISED OF THE POSSIBILITY OF SUCH DAMAGE.
+
+Consecutive cells are adjacent for every grid whose sides are powers of two
+(and for most others).  Host-side utility: the attention call takes the
 resulting permutation as an array.
 """
 from __future__ import annotations

@@ -218,24 +218,32 @@ class Step:
                 events[i + 1].record()
 
 
-def timed_steps(steps_by_set, n_steps, warmup):
+def timed_steps(steps_by_set, n_steps, warmup, every=4):
     """Warm up, then time n_steps passes rotating over the input sets: wall
-    time, and per-unit durations (seconds, one row per step) from events on
-    the launch stream."""
+    time, per-unit durations (seconds, one row per sampled step) from events
+    on the launch stream around every call of every `every`-th step (an event
+    pair costs about a microsecond of stream time, so the other steps run
+    without them), and the GPU span from the first step's start to the last
+    step's end."""
     import torch
     for i in range(warmup):
         steps_by_set[i % len(steps_by_set)].run()
     torch.cuda.synchronize()
     n_units = len(steps_by_set[0].calls)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_units + 1)] for _ in range(n_steps)]
+    sampled = [i for i in range(n_steps) if i % every == 0]
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(n_units + 1)] for i in sampled}
+    first = torch.cuda.Event(enable_timing=True)
+    last = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    first.record()
     for i in range(n_steps):
-        steps_by_set[i % len(steps_by_set)].run(ev[i])
+        steps_by_set[i % len(steps_by_set)].run(ev.get(i))
+    last.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(n_units)] for e in ev]) * 1e-3
-    span = ev[0][0].elapsed_time(ev[-1][-1]) * 1e-3
+    per = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(n_units)] for i in sampled]) * 1e-3
+    span = first.elapsed_time(last) * 1e-3
     return wall, per, span
 
 
@@ -279,7 +287,7 @@ def complexity(args):
                  "Y": torch.empty((B, H, N, d), dtype=torch.float32, device=dev),
                  "ws": torch.empty(_lib.workspace_size(B, H, d, M0, C, torch.bfloat16), dtype=torch.uint8,
                                    device=dev)}
-            _, per, _ = timed_steps([Step(cfg, P, s, stream)], steps, warm)
+            _, per, _ = timed_steps([Step(cfg, P, s, stream)], steps, warm, every=1)
             k1 = float(np.median(per[:, 0])) * 1e6
             k2 = float(np.median(per[:, 1] + per[:, 2])) * 1e6
             rows.append({"N": N, "kind": kind, "M0": M0, "C": C, "P": P, "precompute_codes": M0 + C,
@@ -523,7 +531,8 @@ def main():
         },
         "units": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in units.items()},
-        "gpu_span_ms_per_step": round(gpu_span / max(1, args.steps - 1) * 1e3, 5),
+        "gpu_span_ms_per_step": round(gpu_span / args.steps * 1e3, 5),
+        "event_sampled_steps": int(per.shape[0]),
         "unit_sum_ms_per_step": round(float(per.sum(axis=1).mean()) * 1e3, 5),
         "Mhead_tokens_per_s": round(cfg.B * cfg.H * cfg.N / (wall / args.steps) / 1e6, 3),
     }
