@@ -49,10 +49,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.avq_attention_fwd_ordered.restype = i32
     lib.avq_attention_fwd_noalloc.argtypes = [P, P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P]
     lib.avq_attention_fwd_noalloc.restype = i32
-    lib.avq_attention_prepare.argtypes = [P] + [i32] * 6 + [P, ctypes.c_size_t, P]
+    lib.avq_assign_aggregate_accum.argtypes = [P, P, P] + [i32] * 7 + [P, P, P, P]
+    lib.avq_assign_aggregate_accum.restype = i32
+    lib.avq_attention_prepare.argtypes = [P, P] + [i32] * 6 + [P, ctypes.c_size_t, P]
     lib.avq_attention_prepare.restype = i32
-    lib.avq_attention_fwd_prepared.argtypes = [P, P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P,
-                                                                     ctypes.c_size_t, P]
+    lib.avq_attention_fwd_prepared.argtypes = [P, P] + [i32] * 7 + [i32, i32, f32, P, P, P, P, ctypes.c_size_t,
+                                                                  P, P, P]
     lib.avq_attention_fwd_prepared.restype = i32
     lib.avq_codebook_update.argtypes = [P, P] + [i32] * 5 + [f32, P, P, P, P]
     lib.avq_codebook_update.restype = i32
@@ -183,6 +185,22 @@ def assign_aggregate(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C
     return vsum, counts, assign
 
 
+def assign_aggregate_accum(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C: int, *,
+                           vsum: torch.Tensor, counts: torch.Tensor, assign: Optional[torch.Tensor] = None):
+    """avq_assign_aggregate_accum: kernel 1 adding this batch's value sums and counts to vsum and
+    counts (given, [B, H, Mt, d] float32 and [B, H, Mt] int32; no zero fill).  Returns (vsum,
+    counts, assign or None)."""
+    if vsum is None or counts is None:
+        raise ValueError("vsum and counts are accumulated into: both must be given")
+    (B, H, N, d, M0), vsum, counts, assign, _ = _assign_args(K, V, codebook, C, vsum, counts, assign, None,
+                                                            assign is not None, False)
+    rc = _lib.avq_assign_aggregate_accum(_ptr(K), _ptr(V), _ptr(codebook), B, H, N, d, M0, C, _dtype_code(K),
+                                         _ptr(vsum), _ptr(counts), _ptr(assign), _stream(K))
+    if rc != 0:
+        raise AvqError(rc, "avq_assign_aggregate_accum")
+    return vsum, counts, assign
+
+
 def assign_aggregate_kv(K: torch.Tensor, V: torch.Tensor, codebook: torch.Tensor, C: int, *,
                         want_assign: bool = False, vsum: Optional[torch.Tensor] = None,
                         counts: Optional[torch.Tensor] = None, assign: Optional[torch.Tensor] = None,
@@ -255,15 +273,17 @@ def attention_fwd(Q: torch.Tensor, codebook: torch.Tensor, vsum: torch.Tensor, c
     return Y, topp, imp
 
 
-def attention_prepare(vsum: torch.Tensor, C: int, dtype: torch.dtype, *,
+def attention_prepare(vsum: torch.Tensor, counts: torch.Tensor, C: int, dtype: torch.dtype, *,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """avq_attention_prepare: the value-sum operands of kernel 2 (Eq. 6 and 9) for this batch's
-    aggregates, written to ``workspace`` (uint8 device tensor, allocated here when not given) and
-    returned for attention_fwd_prepared.  ``dtype`` is the dtype of the queries and codebook."""
+    """avq_attention_prepare: the value-sum operands of kernel 2 (Eq. 6 and 9) and a copy of the
+    counts for this batch's aggregates, written to ``workspace`` (uint8 device tensor, allocated
+    here when not given) and returned for attention_fwd_prepared.  ``dtype`` is the dtype of the
+    queries and codebook."""
     if not isinstance(vsum, torch.Tensor) or vsum.dim() != 4:
         raise ValueError("vsum must be a float32 [B, H, Mt, d] tensor")
     B, H, Mt, d = (int(x) for x in vsum.shape)
     _check(vsum, "vsum", (B, H, Mt, d), torch.float32)
+    _check(counts, "counts", (B, H, Mt), torch.int32)
     if not isinstance(C, int) or C < 0 or Mt == 0 or Mt % (1 + C):
         raise ValueError(f"codeword rows ({Mt}) must be M0 * (1 + C) with C >= 0, C = {C!r}")
     if dtype not in (torch.float32, torch.bfloat16):
@@ -271,11 +291,11 @@ def attention_prepare(vsum: torch.Tensor, C: int, dtype: torch.dtype, *,
     M0 = Mt // (1 + C)
     if workspace is not None:
         _check(workspace, "workspace", None, torch.uint8)
-    _on_device([("vsum", vsum), ("workspace", workspace)])
+    _on_device([("vsum", vsum), ("counts", counts), ("workspace", workspace)])
     need = workspace_size(B, H, d, M0, C, dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=vsum.device)
-    rc = _lib.avq_attention_prepare(_ptr(vsum), B, H, d, M0, C,
+    rc = _lib.avq_attention_prepare(_ptr(vsum), _ptr(counts), B, H, d, M0, C,
                                     AVQ_BF16 if dtype == torch.bfloat16 else AVQ_F32, _ptr(workspace),
                                     workspace.numel(), _stream(vsum))
     if rc != 0:
@@ -283,25 +303,28 @@ def attention_prepare(vsum: torch.Tensor, C: int, dtype: torch.dtype, *,
     return workspace
 
 
-def attention_fwd_prepared(Q: torch.Tensor, codebook: torch.Tensor, counts: torch.Tensor, workspace: torch.Tensor,
-                           C: int, P: int, block_q: int, scale: Optional[float] = None, *, want_topp: bool = False,
+def attention_fwd_prepared(Q: torch.Tensor, codebook: torch.Tensor, workspace: torch.Tensor, C: int, P: int,
+                           block_q: int, scale: Optional[float] = None, *, want_topp: bool = False,
                            want_importance: bool = False, Y: Optional[torch.Tensor] = None,
-                           topp: Optional[torch.Tensor] = None, importance: Optional[torch.Tensor] = None):
+                           topp: Optional[torch.Tensor] = None, importance: Optional[torch.Tensor] = None,
+                           clear_vsum: Optional[torch.Tensor] = None, clear_counts: Optional[torch.Tensor] = None):
     """avq_attention_fwd_prepared: the attention kernel alone, on a workspace that attention_prepare
     filled for the same aggregates.  Returns (Y, topp or None, importance or None) like attention_fwd;
-    outputs given as tensors are written in place (nothing is allocated then)."""
+    outputs given as tensors are written in place (nothing is allocated then).  ``clear_vsum`` /
+    ``clear_counts`` ([B, H, Mt, d] float32 / [B, H, Mt] int32) are zero-filled by the call."""
     B, H, N, d = _shape4(Q, "Q")
     dev = Q.device
     Mt, M0 = _codebook_rows(codebook, H, d, Q.dtype, C)
     T = (N + block_q - 1) // block_q if block_q > 0 else 0
-    _check(counts, "counts", (B, H, Mt), torch.int32)
     _check(workspace, "workspace", None, torch.uint8)
     for name, t, shape, dt in (("Y", Y, (B, H, N, d), torch.float32), ("topp", topp, (B, H, T, P), torch.int32),
-                               ("importance", importance, (B, H, T, M0), torch.float32)):
+                               ("importance", importance, (B, H, T, M0), torch.float32),
+                               ("clear_vsum", clear_vsum, (B, H, Mt, d), torch.float32),
+                               ("clear_counts", clear_counts, (B, H, Mt), torch.int32)):
         if t is not None:
             _check(t, name, shape, dt)
-    _on_device([("Q", Q), ("codebook", codebook), ("counts", counts), ("workspace", workspace), ("Y", Y),
-                ("topp", topp), ("importance", importance)])
+    _on_device([("Q", Q), ("codebook", codebook), ("workspace", workspace), ("Y", Y), ("topp", topp),
+                ("importance", importance), ("clear_vsum", clear_vsum), ("clear_counts", clear_counts)])
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     if Y is None:
@@ -310,9 +333,9 @@ def attention_fwd_prepared(Q: torch.Tensor, codebook: torch.Tensor, counts: torc
         topp = torch.empty((B, H, T, P), dtype=torch.int32, device=dev)
     if importance is None and want_importance:
         importance = torch.empty((B, H, T, M0), dtype=torch.float32, device=dev)
-    rc = _lib.avq_attention_fwd_prepared(_ptr(Q), _ptr(codebook), _ptr(counts), B, H, N, d, M0, C, _dtype_code(Q),
-                                         P, block_q, float(scale), _ptr(Y), _ptr(topp), _ptr(importance),
-                                         _ptr(workspace), workspace.numel(), _stream(Q))
+    rc = _lib.avq_attention_fwd_prepared(_ptr(Q), _ptr(codebook), B, H, N, d, M0, C, _dtype_code(Q), P, block_q,
+                                         float(scale), _ptr(Y), _ptr(topp), _ptr(importance), _ptr(workspace),
+                                         workspace.numel(), _ptr(clear_vsum), _ptr(clear_counts), _stream(Q))
     if rc != 0:
         raise AvqError(rc, "avq_attention_fwd_prepared")
     return Y, topp, importance

@@ -54,8 +54,11 @@ hipError_t raise_lds_limit(const void* kernel, size_t bytes) {
 
 namespace {
 
+// zero: fill vsum, counts (and ksum) with zeros first; else add this batch's
+// sums and counts to what they hold
 int assign_call(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0, int C,
-                int dtype, float* vsum, int32_t* counts, int32_t* assign, float* ksum, bool with_keys, void* stream) {
+                int dtype, float* vsum, int32_t* counts, int32_t* assign, float* ksum, bool with_keys, void* stream,
+                bool zero = true) {
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
   const int64_t BH = (int64_t)B * H;
@@ -68,9 +71,12 @@ int assign_call(const void* K, const void* V, const void* codebook, int B, int H
   if (avq::assign_smem_bytes(dtype, d, M0, C) > (size_t)kMaxLds) return AVQ_ERR_UNSUPPORTED;
   const int64_t Mt = (int64_t)M0 * (1 + C);
   hipStream_t st = (hipStream_t)stream;
-  rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, with_keys ? ksum : nullptr, with_keys ? BH * Mt * d : 0, counts,
-                                 BH * Mt, st));
-  if (rc != AVQ_OK || N == 0) return rc;
+  if (zero) {
+    rc = from_hip(avq::launch_zero(vsum, BH * Mt * d, with_keys ? ksum : nullptr, with_keys ? BH * Mt * d : 0, counts,
+                                   BH * Mt, st));
+    if (rc != AVQ_OK) return rc;
+  }
+  if (N == 0) return AVQ_OK;
   return from_hip(avq::launch_assign(dtype, K, V, codebook, (int)BH, H, N, d, M0, C, vsum, counts, assign,
                                      with_keys ? ksum : nullptr, st));
 }
@@ -82,6 +88,11 @@ extern "C" {
 int avq_assign_aggregate(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0, int C,
                          int dtype, float* vsum, int32_t* counts, int32_t* assign, void* stream) {
   return assign_call(K, V, codebook, B, H, N, d, M0, C, dtype, vsum, counts, assign, nullptr, false, stream);
+}
+
+int avq_assign_aggregate_accum(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0,
+                               int C, int dtype, float* vsum, int32_t* counts, int32_t* assign, void* stream) {
+  return assign_call(K, V, codebook, B, H, N, d, M0, C, dtype, vsum, counts, assign, nullptr, false, stream, false);
 }
 
 int avq_assign_aggregate_kv(const void* K, const void* V, const void* codebook, int B, int H, int N, int d, int M0,
@@ -99,14 +110,16 @@ size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C, int dtyp
 
 namespace {
 
-// stages: avq::kAttnPrep (value fragments from vsum into the workspace) and/or
-// avq::kAttnKernel (the attention kernel, from a prepared workspace); vsum is
-// needed by the first, Q, codebook, counts and Y by the second
+// stages: avq::kAttnPrep (value fragments from vsum, and a copy of counts,
+// into the workspace) and/or avq::kAttnKernel (the attention kernel, from a
+// prepared workspace, optionally zero-filling clear_v and clear_c); vsum and
+// counts are needed by the first, Q, codebook and Y by the second
 int attention_call(const void* Q, const void* codebook, const float* vsum, const int32_t* counts, int B, int H, int N,
                    int d, int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
                    float* importance, void* workspace, size_t workspace_bytes, void* stream, bool approx,
                    const int32_t* order, bool ordered, bool validate_only = false,
-                   int stages = avq::kAttnPrep | avq::kAttnKernel) {
+                   int stages = avq::kAttnPrep | avq::kAttnKernel, float* clear_v = nullptr,
+                   int32_t* clear_c = nullptr) {
   const bool prep = (stages & avq::kAttnPrep) != 0, kern = (stages & avq::kAttnKernel) != 0;
   int rc = check_common(B, H, N, d, M0, C, dtype);
   if (rc != AVQ_OK) return rc;
@@ -116,11 +129,20 @@ int attention_call(const void* Q, const void* codebook, const float* vsum, const
     if (!isfinite(scale) || !(scale > 0.0f)) return AVQ_ERR_SHAPE;
   }
   const int64_t BH = (int64_t)B * H;
-  if (BH == 0 || (kern && N == 0)) return AVQ_OK;
-  if (!workspace || (prep && !vsum) || (kern && (!Q || !codebook || !counts || !Y || (ordered && !order))))
+  if (BH == 0) return AVQ_OK;
+  if (kern && N == 0) {  // no queries: nothing to attend, only the requested clearing
+    if (!clear_v && !clear_c) return AVQ_OK;
+    if ((clear_v && !aligned16(clear_v)) || (clear_c && !aligned16(clear_c))) return AVQ_ERR_ALIGN;
+    if (validate_only) return AVQ_OK;
+    const int64_t Mt = (int64_t)M0 * (1 + C);
+    return from_hip(avq::launch_zero(clear_v, clear_v ? BH * Mt * d : 0, nullptr, 0, clear_c, clear_c ? BH * Mt : 0,
+                                     (hipStream_t)stream));
+  }
+  if (!workspace || (prep && (!vsum || !counts)) || (kern && (!Q || !codebook || !Y || (ordered && !order))))
     return AVQ_ERR_NULL;
   if ((Q && !aligned16(Q)) || (codebook && !aligned16(codebook)) || (vsum && !aligned16(vsum)) ||
-      (counts && !aligned16(counts)) || (Y && !aligned16(Y)) || !aligned16(workspace) || (topp && !aligned16(topp)) ||
+      (counts && !aligned16(counts)) || (Y && !aligned16(Y)) || (clear_v && !aligned16(clear_v)) ||
+      (clear_c && !aligned16(clear_c)) || !aligned16(workspace) || (topp && !aligned16(topp)) ||
       (importance && !aligned16(importance)) || ((uintptr_t)order & 3u) != 0)
     return AVQ_ERR_ALIGN;
   if (workspace_bytes < avq::attention_workspace_bytes(dtype, d, M0, C, (int)BH)) return AVQ_ERR_WORKSPACE;
@@ -128,7 +150,8 @@ int attention_call(const void* Q, const void* codebook, const float* vsum, const
     return AVQ_ERR_UNSUPPORTED;
   if (validate_only) return AVQ_OK;
   return from_hip(avq::launch_attention(dtype, Q, codebook, vsum, counts, (int)BH, H, N, d, M0, C, P, block_q, scale,
-                                        Y, topp, importance, workspace, approx, order, stages, (hipStream_t)stream));
+                                        Y, topp, importance, workspace, approx, order, stages, clear_v, clear_c,
+                                        (hipStream_t)stream));
 }
 
 }  // namespace
@@ -158,18 +181,19 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
                         workspace, workspace_bytes, stream, approx_denominator != 0, query_order, true);
 }
 
-int avq_attention_prepare(const float* vsum, int B, int H, int d, int M0, int C, int dtype, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  return attention_call(nullptr, nullptr, vsum, nullptr, B, H, 0, d, M0, C, dtype, 0, 32, 1.0f, nullptr, nullptr, nullptr,
-                        workspace, workspace_bytes, stream, false, nullptr, false, false, avq::kAttnPrep);
+int avq_attention_prepare(const float* vsum, const int32_t* counts, int B, int H, int d, int M0, int C, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_call(nullptr, nullptr, vsum, counts, B, H, 0, d, M0, C, dtype, 0, 32, 1.0f, nullptr, nullptr,
+                        nullptr, workspace, workspace_bytes, stream, false, nullptr, false, false, avq::kAttnPrep);
 }
 
-int avq_attention_fwd_prepared(const void* Q, const void* codebook, const int32_t* counts, int B, int H, int N, int d,
-                               int M0, int C, int dtype, int P, int block_q, float scale, float* Y, int32_t* topp,
-                               float* importance, const void* workspace, size_t workspace_bytes, void* stream) {
-  return attention_call(Q, codebook, nullptr, counts, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp, importance,
-                        const_cast<void*>(workspace), workspace_bytes, stream, false, nullptr, false, false,
-                        avq::kAttnKernel);
+int avq_attention_fwd_prepared(const void* Q, const void* codebook, int B, int H, int N, int d, int M0, int C,
+                               int dtype, int P, int block_q, float scale, float* Y, int32_t* topp, float* importance,
+                               const void* workspace, size_t workspace_bytes, float* clear_vsum,
+                               int32_t* clear_counts, void* stream) {
+  return attention_call(Q, codebook, nullptr, nullptr, B, H, N, d, M0, C, dtype, P, block_q, scale, Y, topp,
+                        importance, const_cast<void*>(workspace), workspace_bytes, stream, false, nullptr, false,
+                        false, avq::kAttnKernel, clear_vsum, clear_counts);
 }
 
 }  // extern "C"

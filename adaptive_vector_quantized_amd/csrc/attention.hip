@@ -107,6 +107,19 @@ __device__ __forceinline__ void lds_dma_buf(__amdgpu_buffer_rsrc_t rs, int voff,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 4, voff, 0, 0, 0);
 }
 
+// Zero fill of the caller's value sums and counts by the attention kernel,
+// spread over its whole grid (plain stores): once the preparation has run,
+// the kernel reads neither, and the next accumulating assignment call adds
+// into them.
+__device__ __forceinline__ void clear_buffers(float* v, int64_t n4, int* c, int64_t nc) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v != nullptr)
+    for (int64_t i = t; i < n4; i += stride) ((f32x4*)v)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (c != nullptr)
+    for (int64_t i = t; i < nc; i += stride) c[i] = 0;
+}
+
 // Top-P of Alg. 2 over the importances one wave holds (parent j = 64 g + lane
 // in u[g]; non-negative floats as bit patterns, so integer order is value
 // order).  A radix search on the bits, from the top, raises a threshold thr
@@ -160,12 +173,14 @@ constexpr int kYRow = 36;  // floats per staged output row (32 dims + 4 to sprea
 
 // Workspace: [BH] value scales | [BH] value operand fragments | [BH][slices]
 // partial maxima of |vsum| (one per slice of kMaxSlice4 float4 of a head's
-// value sums).
+// value sums) | [BH][Mt] a copy of the counts (the attention kernel reads
+// the counts from here, so that the caller's counts are free once the
+// preparation has run).
 constexpr int kMaxThreads = 256;               // threads of the partial-maximum kernel
 constexpr int kMaxPer = 4;                     // float4 loads per thread
 constexpr int kMaxSlice4 = kMaxThreads * kMaxPer;
 struct AttnWs {
-  size_t sig_bytes, per_bh, pmax_off, total;
+  size_t sig_bytes, per_bh, pmax_off, counts_off, total;
   int slices;
 };
 static AttnWs attn_ws(int dtype, int d, int M0, int C, int BH) {
@@ -178,7 +193,8 @@ static AttnWs attn_ws(int dtype, int d, int M0, int C, int BH) {
   w.per_bh = align256((M0p * d + (size_t)M0 * W * d) * pes);
   w.slices = (int)((n4 + kMaxSlice4 - 1) / kMaxSlice4);
   w.pmax_off = w.sig_bytes + (size_t)BH * w.per_bh;
-  w.total = w.pmax_off + align256((size_t)BH * w.slices * 4);
+  w.counts_off = w.pmax_off + align256((size_t)BH * w.slices * 4);
+  w.total = w.counts_off + align256((size_t)BH * M0 * (1 + C) * 4);
   return w;
 }
 
@@ -224,10 +240,12 @@ __global__ __launch_bounds__(kMaxThreads) void attention_absmax_kernel(const flo
 }
 
 template <class T, int D, int W>
-__global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const float* __restrict__ vsum, int BH, int M0,
+__global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const float* __restrict__ vsum,
+                                                                      const int* __restrict__ counts, int BH, int M0,
                                                                       int C, int parts, unsigned char* __restrict__ ws,
                                                                       size_t sig_bytes, size_t per_bh,
-                                                                      const float* __restrict__ pmax, int slices) {
+                                                                      const float* __restrict__ pmax, int slices,
+                                                                      int* __restrict__ counts_copy) {
   using pvfrag_t = typename T::pvfrag_t;
   constexpr int E = T::E;
   constexpr int KV = 16 / E;
@@ -251,6 +269,9 @@ __global__ __launch_bounds__(kPrepThreads) void attention_prep_kernel(const floa
   const int Mt = M0 * (1 + C);
   const int M0p = attn_parent_rows(M0);
   const float* vs = vsum + (int64_t)bh * Mt * D;
+  // this block's share of the head's counts, copied for the attention kernel
+  for (int i = part * kPrepThreads + tid; i < Mt; i += parts * kPrepThreads)
+    counts_copy[(int64_t)bh * Mt + i] = counts[(int64_t)bh * Mt + i];
   const int nP = (M0p / 32) * KV * 2 * D;           // parent fragments
   const int nF = nP + (C > 0 ? M0 * (W / E) * D : 0);  // + child fragments
   // gathers of this thread's fragments (unscaled)
@@ -327,7 +348,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
     const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
     int bq, int tiles_per_wg, int wgs_per_bh, float sl2, float* __restrict__ Y, int* __restrict__ topp,
-    float* __restrict__ importance, int approx, const int* __restrict__ order) {
+    float* __restrict__ importance, int approx, const int* __restrict__ order, float* __restrict__ clear_v,
+    int64_t clear_v4, int* __restrict__ clear_c, int64_t clear_nc) {
   using in_t = typename T::in_t;
   using frag_t = typename T::frag_t;
   using pvfrag_t = typename T::pvfrag_t;
@@ -388,6 +410,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       g = L % wgs_per_bh;
     }
   }
+  // this workgroup's share of the requested zero fill, first (measured: it
+  // costs least issued before anything else)
+  clear_buffers(clear_v, clear_v4, clear_c, clear_nc);
   const int h = bh % H;
   const int ntiles = (N + bq - 1) / bq;
   const int tile0 = g * tiles_per_wg;
@@ -919,7 +944,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const typename T::in_t* __restrict__ Q, const typename T::in_t* __restrict__ cb, const int* __restrict__ counts,
     const unsigned char* __restrict__ ws, size_t sig_bytes, size_t per_bh, int H, int BH, int N, int M0, int C, int P,
     int bq, int tiles_per_wg, int wgs_per_bh, float sl2, float* __restrict__ Y, int* __restrict__ topp,
-    float* __restrict__ importance, const int* __restrict__ order) {
+    float* __restrict__ importance, const int* __restrict__ order, float* __restrict__ clear_v, int64_t clear_v4,
+    int* __restrict__ clear_c, int64_t clear_nc) {
   using in_t = typename T::in_t;
   using frag_t = typename T::frag_t;
   using pvfrag_t = typename T::pvfrag_t;
@@ -969,6 +995,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
       g = L % wgs_per_bh;
     }
   }
+  // this workgroup's share of the requested zero fill, first (measured: it
+  // costs least issued before anything else)
+  clear_buffers(clear_v, clear_v4, clear_c, clear_nc);
   const int h = bh % H;
   const int ntiles = (N + bq - 1) / bq;
   const int tile0 = g * tiles_per_wg;
@@ -1397,7 +1426,7 @@ int attention_tiles_per_wg(int BH, int N, int bq) {
 template <class T, int D, int W, bool PL, bool VL>
 static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, const int* order, int stages, hipStream_t st) {
+                                void* ws, bool approx, const int* order, int stages, float* clear_v, int* clear_c, hipStream_t st) {
   const int dtype = std::is_same<T, TF32>::value ? 0 : 1;
   const AttnWs wl = attn_ws(dtype, D, M0, C, BH);
   const size_t sig_bytes = wl.sig_bytes, per_bh = wl.per_bh;
@@ -1416,12 +1445,17 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, BH, M0,
-                       C, parts, (unsigned char*)ws, sig_bytes, per_bh, (const float*)pmax, wl.slices);
+    hipLaunchKernelGGL((attention_prep_kernel<T, D, W>), dim3(BH * parts), dim3(kPrepThreads), 0, st, vsum, counts,
+                       BH, M0, C, parts, (unsigned char*)ws, sig_bytes, per_bh, (const float*)pmax, wl.slices,
+                       (int*)((unsigned char*)ws + wl.counts_off));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!(stages & kAttnKernel)) return hipSuccess;
+  // the kernel reads the counts from the workspace copy the preparation made
+  const int* wcounts = (const int*)((const unsigned char*)ws + wl.counts_off);
+  const int64_t Mt = (int64_t)M0 * (1 + C);
+  const int64_t clear_v4 = clear_v ? (int64_t)BH * Mt * D / 4 : 0, clear_nc = clear_c ? (int64_t)BH * Mt : 0;
   const int tpw = attention_tiles_per_wg(BH, N, bq);
   const int T_ = (N + bq - 1) / bq;
   const int per = (T_ + tpw - 1) / tpw;
@@ -1434,8 +1468,9 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
       hipError_t e = raise_lds_limit((const void*)kern, smem);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
-                         (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N,
-                         M0, C, P, bq, tpw, per, sl2, Y, topp, importance, order);
+                         (const typename T::in_t*)cb, wcounts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH,
+                         N, M0, C, P, bq, tpw, per, sl2, Y, topp, importance, order, clear_v, clear_v4, clear_c,
+                         clear_nc);
       return hipGetLastError();
     }
   }
@@ -1444,18 +1479,19 @@ static hipError_t launch_attn_t(const void* Q, const void* cb, const float* vsum
   hipError_t e = raise_lds_limit((const void*)kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(per * BH), dim3(2 * bq), smem, st, (const typename T::in_t*)Q,
-                     (const typename T::in_t*)cb, counts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N, M0, C,
-                     P, bq, tpw, per, sl2, Y, topp, importance, approx ? 1 : 0, order);
+                     (const typename T::in_t*)cb, wcounts, (const unsigned char*)ws, sig_bytes, per_bh, H, BH, N, M0,
+                     C, P, bq, tpw, per, sl2, Y, topp, importance, approx ? 1 : 0, order, clear_v, clear_v4, clear_c,
+                     clear_nc);
   return hipGetLastError();
 }
 
 template <class T, int D, int W>
 static hipError_t launch_attn_v(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, const int* order, int stages, hipStream_t st) {
+                                void* ws, bool approx, const int* order, int stages, float* clear_v, int* clear_c, hipStream_t st) {
   if (M0 <= 64)
     return launch_attn_t<T, D, W, true, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
-                                              ws, approx, order, stages, st);
+                                              ws, approx, order, stages, clear_v, clear_c, st);
   // at d = 64 the values stay in LDS up to 256 parents; beyond, LDS-resident
   // values would leave one workgroup per CU, with nothing to cover the
   // staged parent passes' barriers (measured at 512 flat codewords: 211 us
@@ -1463,32 +1499,32 @@ static hipError_t launch_attn_v(const void* Q, const void* cb, const float* vsum
   if constexpr (D == 64) {
     if (M0 <= 256)
       return launch_attn_t<T, D, W, false, true>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp,
-                                                 importance, ws, approx, order, stages, st);
+                                                 importance, ws, approx, order, stages, clear_v, clear_c, st);
   }
   return launch_attn_t<T, D, W, false, false>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance,
-                                              ws, approx, order, stages, st);
+                                              ws, approx, order, stages, clear_v, clear_c, st);
 }
 
 template <class T, int D>
 static hipError_t launch_attn_w(const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H, int N,
                                 int M0, int C, int P, int bq, float scale, float* Y, int* topp, float* importance,
-                                void* ws, bool approx, const int* order, int stages, hipStream_t st) {
+                                void* ws, bool approx, const int* order, int stages, float* clear_v, int* clear_c, hipStream_t st) {
   if (C <= 8)
     return launch_attn_v<T, D, 8>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx,
-                                  order, stages, st);
+                                  order, stages, clear_v, clear_c, st);
   return launch_attn_v<T, D, 16>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx,
-                                 order, stages, st);
+                                 order, stages, clear_v, clear_c, st);
 }
 
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, bool approx, const int* order, int stages, hipStream_t st) {
+                            float* importance, void* ws, bool approx, const int* order, int stages, float* clear_v, int* clear_c, hipStream_t st) {
   if (dtype == 0) {
-    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
-    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
+    if (d == 64) return launch_attn_w<TF32, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, clear_v, clear_c, st);
+    return launch_attn_w<TF32, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, clear_v, clear_c, st);
   }
-  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
-  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, st);
+  if (d == 64) return launch_attn_w<TBF16, 64>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, clear_v, clear_c, st);
+  return launch_attn_w<TBF16, 128>(Q, cb, vsum, counts, BH, H, N, M0, C, P, bq, scale, Y, topp, importance, ws, approx, order, stages, clear_v, clear_c, st);
 }
 
 }  // namespace avq

@@ -35,7 +35,8 @@ constexpr int kAttnPrep = 1;
 constexpr int kAttnKernel = 2;
 hipError_t launch_attention(int dtype, const void* Q, const void* cb, const float* vsum, const int* counts, int BH, int H,
                             int N, int d, int M0, int C, int P, int bq, float scale, float* Y, int* topp,
-                            float* importance, void* ws, bool approx, const int* order, int stages, hipStream_t st);
+                            float* importance, void* ws, bool approx, const int* order, int stages, float* clear_v,
+                            int* clear_c, hipStream_t st);
 hipError_t launch_codebook_update(const float* ksum, const int* counts, int B, int H, int d, int M0, int C,
                                   float decay, float* S, float* Nm, float* cb, hipStream_t st);
 

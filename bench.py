@@ -3,12 +3,17 @@
 
 One step = one pass of the whole hot path over one batch, through the C
 interface, on synthetic inputs already resident in HBM:
-  avq_assign_aggregate        zero fill + two-level assignment + value sums
-                              and counts (Sec. 4.2, Alg. 1, Eq. 3)
-  avq_attention_prepare       the value sums as fp16 operand fragments
+  avq_assign_aggregate_accum  two-level assignment + value sums and counts
+                              (Sec. 4.2, Alg. 1, Eq. 3), added into buffers
+                              that hold zeros
+  avq_attention_prepare       the value sums as fp16 operand fragments, and a
+                              copy of the counts
   avq_attention_fwd_prepared  the attention kernel: parent attention,
                               importance, top-P, child correction, output
-                              (Sec. 4.3, Alg. 2, Eq. 6-9)
+                              (Sec. 4.3, Alg. 2, Eq. 6-9); it also zero-fills
+                              the value sums and counts it no longer reads,
+                              for the next step's accumulation (the zero fill
+                              of Alg. 1's first step, moved there)
 The three calls are issued with their arguments marshalled once (ctypes
 argument tuples built before the timed loop), so the timed loop adds no
 Python-side checking between launches.  Three input sets are rotated (larger
@@ -52,6 +57,9 @@ CALLS = {
     "avq_assign_aggregate": ("zero_kernel + assign_aggregate_kernel",
                              ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
                               "adaptive_vector_quantized_amd/csrc/avq_device.h"]),
+    "avq_assign_aggregate_accum": ("assign_aggregate_kernel",
+                                   ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
+                                    "adaptive_vector_quantized_amd/csrc/avq_device.h"]),
     "avq_attention_prepare": ("attention_prep_kernel", _ATTN_SRC),
     "avq_attention_fwd_prepared": ("attention_kernel (or attention_pipe_kernel)", _ATTN_SRC),
     "avq_attention_fwd": ("attention_prep_kernel + attention_kernel", _ATTN_SRC),
@@ -72,6 +80,8 @@ def algorithmic(cfg, P):
     avq_assign_aggregate: read K and V once, the head codebooks once, write
     the value sums and counts once; flops 2 d (M0 + C) per key (parent and
     child distances).
+    avq_assign_aggregate_accum: the same bytes and flops (the aggregates are
+    read-modify-written by atomics in L2; counted once, as written).
     avq_attention_prepare: read the value sums (float) once, write them once
     as operands (fp16 for bf16 inputs, float for fp32 inputs).
     avq_attention_fwd_prepared (the attention kernel): read Q once, write Y
@@ -91,6 +101,7 @@ def algorithmic(cfg, P):
     k1_flops = 2.0 * d * (M0 + C) * BH * N
     k2_flops = 4.0 * d * (M0 + P * C) * BH * N
     return {"avq_assign_aggregate": (k1_bytes, k1_flops),
+            "avq_assign_aggregate_accum": (k1_bytes, k1_flops),
             "avq_attention_prepare": (BH * Mt * d * 4 + operands, 0.0),
             "avq_attention_fwd_prepared": (kern_bytes, k2_flops),
             "avq_attention_fwd": (k2_bytes, k2_flops)}
@@ -163,10 +174,11 @@ def cpu_baseline(cfg, P, runs: int = 3):
 class Step:
     """The C calls of one pass over one input set (a dict of device tensors:
     K, V, Q, cb, vsum, counts, Y, ws), with their ctypes arguments built once,
-    after one checked call through the binding.  With approx or qorder the
-    attention is one call of avq_attention_fwd_approx / _ordered (preparation
-    included); otherwise it is avq_attention_prepare then
-    avq_attention_fwd_prepared."""
+    after one checked call of each through the binding.  With approx or qorder
+    the pass is avq_assign_aggregate then one call of
+    avq_attention_fwd_approx / _ordered (preparation included); otherwise it
+    is avq_assign_aggregate_accum, avq_attention_prepare and
+    avq_attention_fwd_prepared clearing the set's value sums and counts."""
 
     def __init__(self, cfg, P, s, stream, approx=False, qorder=None, block_q=None):
         import ctypes
@@ -180,11 +192,11 @@ class Step:
         shp = (cfg.B, cfg.H, cfg.N, cfg.d, cfg.M0, cfg.C, dt)
         # one checked call of each through the binding (shapes, dtypes, devices)
         _lib.assign_aggregate(s["K"], s["V"], s["cb"], cfg.C, vsum=s["vsum"], counts=s["counts"])
-        self.calls = [("avq_assign_aggregate", L.avq_assign_aggregate,
-                       (ptr(s["K"]), ptr(s["V"]), ptr(s["cb"])) + shp + (ptr(s["vsum"]), ptr(s["counts"]), None, st))]
+        kargs = (ptr(s["K"]), ptr(s["V"]), ptr(s["cb"])) + shp + (ptr(s["vsum"]), ptr(s["counts"]), None, st)
         wsb = s["ws"].numel()
         tail = (P, bq, float(cfg.scale))
         if approx or qorder is not None:
+            self.calls = [("avq_assign_aggregate", L.avq_assign_aggregate, kargs)]
             _lib.attention_fwd(s["Q"], s["cb"], s["vsum"], s["counts"], cfg.C, P, bq, cfg.scale, Y=s["Y"],
                                workspace=s["ws"], approx_denominator=approx, query_order=qorder)
             if qorder is not None:
@@ -196,13 +208,18 @@ class Step:
                     ptr(s["Y"]), None, None, ptr(s["ws"]), wsb, st)
                 self.calls.append(("avq_attention_fwd", L.avq_attention_fwd_approx, args))
         else:
-            _lib.attention_prepare(s["vsum"], cfg.C, s["Q"].dtype, workspace=s["ws"])
-            _lib.attention_fwd_prepared(s["Q"], s["cb"], s["counts"], s["ws"], cfg.C, P, bq, cfg.scale, Y=s["Y"])
-            self.calls.append(("avq_attention_prepare", L.avq_attention_prepare,
-                               (ptr(s["vsum"]), cfg.B, cfg.H, cfg.d, cfg.M0, cfg.C, dt, ptr(s["ws"]), wsb, st)))
-            self.calls.append(("avq_attention_fwd_prepared", L.avq_attention_fwd_prepared,
-                               (ptr(s["Q"]), ptr(s["cb"]), ptr(s["counts"])) + shp + tail + (
-                                   ptr(s["Y"]), None, None, ptr(s["ws"]), wsb, st)))
+            # the checked calls leave the set's value sums and counts zero, as
+            # every step does for the next one
+            _lib.attention_prepare(s["vsum"], s["counts"], cfg.C, s["Q"].dtype, workspace=s["ws"])
+            _lib.attention_fwd_prepared(s["Q"], s["cb"], s["ws"], cfg.C, P, bq, cfg.scale, Y=s["Y"],
+                                        clear_vsum=s["vsum"], clear_counts=s["counts"])
+            self.calls = [("avq_assign_aggregate_accum", L.avq_assign_aggregate_accum, kargs),
+                          ("avq_attention_prepare", L.avq_attention_prepare,
+                           (ptr(s["vsum"]), ptr(s["counts"]), cfg.B, cfg.H, cfg.d, cfg.M0, cfg.C, dt, ptr(s["ws"]),
+                            wsb, st)),
+                          ("avq_attention_fwd_prepared", L.avq_attention_fwd_prepared,
+                           (ptr(s["Q"]), ptr(s["cb"])) + shp + tail + (
+                               ptr(s["Y"]), None, None, ptr(s["ws"]), wsb, ptr(s["vsum"]), ptr(s["counts"]), st))]
         self.names = [c[0] for c in self.calls]
 
     def run(self, events=None):

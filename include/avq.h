@@ -115,11 +115,24 @@ int avq_assign_aggregate_kv(const void* K, const void* V, const void* codebook, 
                             int32_t* counts, int32_t* assign, float* ksum, void* stream);
 
 /*
+ * avq_assign_aggregate without the zero fill: this batch's value sums and
+ * counts (Eq. 3) are added to what vsum and counts already hold, so several
+ * batches of keys, or the keys of one sequence given in parts, accumulate
+ * into one set of aggregates (the sums of Eq. 3 over the union of the
+ * batches).  Every argument, layout and error is that of
+ * avq_assign_aggregate; the caller zero-fills vsum and counts before the
+ * first batch (avq_attention_fwd_prepared can do it as it consumes them).
+ */
+int avq_assign_aggregate_accum(const void* K, const void* V, const void* codebook, int B,
+                               int H, int N, int d, int M0, int C, int dtype, float* vsum,
+                               int32_t* counts, int32_t* assign, void* stream);
+
+/*
  * Bytes of device workspace avq_attention_fwd needs for these sizes (0 if the
  * sizes are invalid).  The workspace holds the value sums of every codeword
- * converted to the operand format of the weighted-value products; it is
- * written and read by one call of avq_attention_fwd and carries nothing
- * between such calls.  avq_attention_prepare and avq_attention_fwd_prepared
+ * converted to the operand format of the weighted-value products and a copy
+ * of the counts; it is written and read by one call of avq_attention_fwd and
+ * carries nothing between such calls.  avq_attention_prepare and avq_attention_fwd_prepared
  * split that call in two around the same workspace.
  */
 size_t avq_attention_workspace_size(int B, int H, int d, int M0, int C,
@@ -228,35 +241,47 @@ int avq_attention_fwd_ordered(const void* Q, const void* codebook, const float* 
 /*
  * The two halves of avq_attention_fwd, for callers that attend several query
  * batches to one set of aggregates (Eq. 3: the value sums and counts depend
- * on the keys only), and to time the attention kernel on its own.
+ * on the keys only), that keep the aggregates' buffers across calls, and to
+ * time the attention kernel on its own.
  *
  * avq_attention_prepare converts the value sums (Eq. 3, from
  * avq_assign_aggregate) into the operands of the weighted-value products
- * (Eq. 6 and 9) and writes them to the workspace: one launch, reading vsum
- * and writing the workspace.  Q, codebook, counts and P play no part, and N
- * is not needed.
+ * (Eq. 6 and 9) and copies the counts, both into the workspace: one or two
+ * launches, reading vsum and counts and writing the workspace.  Q, codebook
+ * and P play no part, and N is not needed.
  *
  * avq_attention_fwd_prepared is then the rest of avq_attention_fwd for one
- * query batch: the attention kernel alone, reading the operands from a
- * workspace that avq_attention_prepare filled with the same B, H, d, M0, C
- * and dtype from the value sums that go with these counts, unchanged since;
- * it does not write the
- * workspace, so any number of such calls may follow one preparation, also
- * concurrently on different streams once the preparation has completed.
- * Given those, its outputs are bit for bit those of avq_attention_fwd on the
- * same arguments.  A workspace not prepared so gives unspecified (but
- * memory-safe) outputs.
+ * query batch: the attention kernel alone, reading the operands and counts
+ * from a workspace that avq_attention_prepare filled with the same B, H, d,
+ * M0, C and dtype, unchanged since; it does not write the workspace, so any
+ * number of such calls may follow one preparation, also concurrently on
+ * different streams once the preparation has completed.  Given those, its
+ * outputs are bit for bit those of avq_attention_fwd on the same arguments.
+ * A workspace not prepared so gives unspecified (but memory-safe) outputs.
  *
- * Arguments, layouts and errors are those of avq_attention_fwd; prepare
- * checks only what it uses (vsum, the workspace and the sizes).
+ *   clear_vsum    NULL, or [B*H, Mt, d] float, 16-byte aligned: zero-filled
+ *                 by the call (every element)
+ *   clear_counts  NULL, or [B*H, Mt] int32, 16-byte aligned: zero-filled
+ * The attention kernel reads neither the value sums nor the counts once they
+ * are prepared, so passing the buffers avq_attention_prepare read leaves them
+ * zero, ready for the next avq_assign_aggregate_accum, with no separate fill
+ * launch (the fill is spread over the attention kernel's workgroups; with
+ * N = 0 the call only fills).  They must not be read or written by other
+ * work in flight meanwhile, and calls sharing one preparation must not clear
+ * a buffer that another of them reads.
+ *
+ * Arguments, layouts and errors are otherwise those of avq_attention_fwd;
+ * prepare checks only what it uses (vsum, counts, the workspace and the
+ * sizes).
  */
-int avq_attention_prepare(const float* vsum, int B, int H, int d, int M0, int C, int dtype,
-                          void* workspace, size_t workspace_bytes, void* stream);
-int avq_attention_fwd_prepared(const void* Q, const void* codebook, const int32_t* counts,
-                               int B, int H, int N, int d, int M0, int C, int dtype,
-                               int P, int block_q, float scale, float* Y, int32_t* topp,
-                               float* importance, const void* workspace,
-                               size_t workspace_bytes, void* stream);
+int avq_attention_prepare(const float* vsum, const int32_t* counts, int B, int H, int d,
+                          int M0, int C, int dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+int avq_attention_fwd_prepared(const void* Q, const void* codebook, int B, int H, int N,
+                               int d, int M0, int C, int dtype, int P, int block_q,
+                               float scale, float* Y, int32_t* topp, float* importance,
+                               const void* workspace, size_t workspace_bytes,
+                               float* clear_vsum, int32_t* clear_counts, void* stream);
 
 /*
  * avq_attention_fwd without a workspace argument, for callers that cannot
@@ -272,8 +297,8 @@ int avq_attention_fwd_prepared(const void* Q, const void* codebook, const int32_
  *
  * Limit: calls whose avq_attention_workspace_size() exceeds
  * AVQ_NOALLOC_SCRATCH_BYTES return AVQ_ERR_SCRATCH and write nothing (bf16,
- * d = 64, M0 = 64, C = 8 fits B*H <= 113; d = 128, M0 = 256, C = 8 fits
- * B*H <= 14).
+ * d = 64, M0 = 64, C = 8 fits B*H <= 110; d = 128, M0 = 256, C = 8 fits
+ * B*H <= 13).
  *
  * Concurrency: every call on one GPU uses that GPU's one scratch array, and
  * each call overwrites what it uses before reading it (nothing carries over

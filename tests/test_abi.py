@@ -21,7 +21,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     from adaptive_vector_quantized_amd import _lib
     names = _lib.declared_symbols()
-    assert set(names) == {"avq_assign_aggregate", "avq_assign_aggregate_kv", "avq_attention_fwd", "avq_attention_fwd_approx",
+    assert set(names) == {"avq_assign_aggregate", "avq_assign_aggregate_kv", "avq_assign_aggregate_accum",
+                          "avq_attention_fwd", "avq_attention_fwd_approx",
                           "avq_attention_fwd_ordered", "avq_attention_fwd_noalloc", "avq_attention_prepare",
                           "avq_attention_fwd_prepared", "avq_attention_workspace_size",
                           "avq_codebook_update", "avq_status_string", "avq_version"}
@@ -51,6 +52,8 @@ def _call_assign(L, kv=False, **kw):
     a.update(kw)
     args = [a["K"], a["V"], a["cb"], a["B"], a["H"], a["N"], a["d"], a["M0"], a["C"], a["dtype"], a["vsum"],
             a["counts"], a["assign"]]
+    if kv == "accum":
+        return L.avq_assign_aggregate_accum(*args, None)
     if kv:
         return L.avq_assign_aggregate_kv(*args, a["ksum"], None)
     return L.avq_assign_aggregate(*args, None)
@@ -66,9 +69,9 @@ def _call_attn(L, fn="avq_attention_fwd", **kw):
                                            a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"],
                                            a["topp"], a["imp"], None)
     if fn == "avq_attention_fwd_prepared":
-        return L.avq_attention_fwd_prepared(a["Q"], a["cb"], a["counts"], a["B"], a["H"], a["N"], a["d"], a["M0"],
-                                            a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"],
-                                            a["imp"], a["ws"], a["wsb"], None)
+        return L.avq_attention_fwd_prepared(a["Q"], a["cb"], a["B"], a["H"], a["N"], a["d"], a["M0"], a["C"],
+                                            a["dtype"], a["P"], a["bq"], a["scale"], a["Y"], a["topp"], a["imp"],
+                                            a["ws"], a["wsb"], a.get("cv"), a.get("cc"), None)
     if fn == "avq_attention_fwd_ordered":
         return L.avq_attention_fwd_ordered(a["Q"], a["cb"], a["vsum"], a["counts"], a["B"], a["H"], a["N"], a["d"],
                                            a["M0"], a["C"], a["dtype"], a["P"], a["bq"], a["scale"], a["order"],
@@ -78,7 +81,7 @@ def _call_attn(L, fn="avq_attention_fwd", **kw):
                           a["ws"], a["wsb"], None)
 
 
-@pytest.mark.parametrize("kv", [False, True])
+@pytest.mark.parametrize("kv", [False, True, "accum"])
 def test_assign_validation(L, kv):
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 4)
@@ -101,7 +104,7 @@ def test_assign_validation(L, kv):
     assert _assign(L, assign=mis) == -4
     assert _assign(L, B=0) == 0       # no (batch, head): nothing to do, nothing launched
     assert _assign(L, H=0, K=None) == 0
-    if kv:
+    if kv is True:
         assert _assign(L, ksum=None) == -1
         assert _assign(L, ksum=mis) == -4
 
@@ -125,7 +128,11 @@ def test_attention_validation(L, fn):
     assert _attn(L, d=32) == -5
     assert _attn(L, Q=None) == -1
     assert _attn(L, Y=None) == -1
-    assert _attn(L, counts=None) == -1
+    if fn != "avq_attention_fwd_prepared":  # (the prepared call reads the workspace's copy of the counts)
+        assert _attn(L, counts=None) == -1
+    else:
+        assert _attn(L, cv=mis) == -4
+        assert _attn(L, cc=ctypes.c_void_p(p.value + 4)) == -4
     assert _attn(L, Y=mis) == -4
     assert _attn(L, topp=mis) == -4
     assert _attn(L, scale=0.0) == -2
@@ -140,23 +147,23 @@ def test_attention_validation(L, fn):
         need = L.avq_attention_workspace_size(1, 200, 64, 64, 8, 1)
         assert need > (8 << 20)
         assert _attn(L, H=200, M0=64, C=8, P=16, bq=128) == -8
-        assert L.avq_attention_workspace_size(1, 113, 64, 64, 8, 1) <= (8 << 20)
+        assert L.avq_attention_workspace_size(1, 110, 64, 64, 8, 1) <= (8 << 20)
     assert L.avq_attention_workspace_size(1, 1, 96, 4, 2, 1) == 0   # invalid sizes
     assert _attn(L, N=0) == 0         # no queries: nothing to do
     assert _attn(L, B=0, Q=None) == 0
 
 
 def test_prepare_validation(L):
-    """avq_attention_prepare checks the sizes, the value sums and the workspace
-    (it reads nothing else)."""
+    """avq_attention_prepare checks the sizes, the value sums, the counts and
+    the workspace (it reads nothing else)."""
     _, p = _buf()
     mis = ctypes.c_void_p(p.value + 8)
 
     def _prep(**kw):
-        a = dict(vsum=p, B=1, H=1, d=64, M0=4, C=2, dtype=1, ws=p, wsb=1 << 30)
+        a = dict(vsum=p, counts=p, B=1, H=1, d=64, M0=4, C=2, dtype=1, ws=p, wsb=1 << 30)
         a.update(kw)
-        return L.avq_attention_prepare(a["vsum"], a["B"], a["H"], a["d"], a["M0"], a["C"], a["dtype"], a["ws"],
-                                       a["wsb"], None)
+        return L.avq_attention_prepare(a["vsum"], a["counts"], a["B"], a["H"], a["d"], a["M0"], a["C"], a["dtype"],
+                                       a["ws"], a["wsb"], None)
     assert _prep(dtype=2) == -3
     assert _prep(B=-1) == -2
     assert _prep(M0=0) == -2
@@ -164,7 +171,9 @@ def test_prepare_validation(L):
     assert _prep(d=32) == -5
     assert _prep(M0=513) == -5
     assert _prep(vsum=None) == -1
+    assert _prep(counts=None) == -1
     assert _prep(ws=None) == -1
+    assert _prep(counts=ctypes.c_void_p(p.value + 4)) == -4
     assert _prep(vsum=mis) == -4
     assert _prep(ws=mis) == -4
     need = L.avq_attention_workspace_size(1, 1, 64, 4, 2, 1)
