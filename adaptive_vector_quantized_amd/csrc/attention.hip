@@ -536,6 +536,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (next >= 0) stage_pass(next);
   };
   if constexpr (!parents_lds) stage_pass(0);
+  // Parents' value fragments that are not held in LDS: with children to
+  // refine, the first pass's value products read them from the two child
+  // buffers (idle until the children, each exactly one 64-parent pass of
+  // value fragments in size), shared by the workgroup's waves, instead of
+  // every wave reading them from L2.  Pass pt uses buffer pt % 2; the copy
+  // of pass pt + 1 is issued right after pass pt's opening barrier (every
+  // wave is then done with pass pt - 1, the buffer's last user) and waited
+  // for by pass pt + 1's opening wait and barrier; only pass 0's own copy
+  // needs a wait of its own.
+  const bool vstage = !values_lds && nCB > 0;
+  pvfrag_t* const vbuf[2] = {sCV, (pvfrag_t*)sCC};
+  auto stage_values = [&](int pt2) {
+    pvfrag_t* dst = vbuf[pt2 & 1];
+    for (int u = wave; u < 2 * FV / 64; u += nw) lds_dma<BV>(pvf + pt2 * 2 * FV + u * 64 + lane, dst + u * 64);
+  };
 
   // ---- query tiles ------------------------------------------------------------
   for (int tile = tile0; tile < tile1; ++tile) {
@@ -572,6 +587,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int pt = 0; pt < nPT; ++pt) {
       const int j0 = pt * 64;
       if constexpr (!parents_lds) wait_pass();
+      if (vstage) {
+        if (pt == 0) stage_values(0);
+        if (pt + 1 < nPT) stage_values(pt + 1);
+      }
       // empty parents and padding rows (count 0) get logit -inf: their bias
       // enters as the initial value of the accumulator (zero when every
       // parent of the pass holds keys)
@@ -620,13 +639,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             zp = fmaf(a, n4[u], zp);
           }
         }
-        const int bb = pt * 2 + b;
+      }
+      if (vstage && pt == 0) {  // pass 0's value fragments have landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      const pvfrag_t* vsrc = vstage ? vbuf[pt & 1] : values_lds ? sPV + pt * 2 * FV : pvf + pt * 2 * FV;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int k = 0; k < KV; ++k) {
           const pvfrag_t bf = pv_operand<T, KV>(lg[b], k);
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            xacc[db] = T::mma_pv((values_lds ? sPV : pvf)[((bb * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
+            xacc[db] = T::mma_pv(vsrc[((b * KV + k) * 2 + hh) * D + ql + 32 * db], bf, xacc[db]);
         }
       }
       if constexpr (!parents_lds) {
