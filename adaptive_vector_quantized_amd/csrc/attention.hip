@@ -380,10 +380,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
   // the children's arrays exist only when P > 0, the importance partials only
   // when importances are formed
   const bool need_imp = (P > 0) || (importance != nullptr);
-  const int nCB = P > 0 ? NCB : 0, nCH = P > 0 ? CH : 0;
+  const int nCH = P > 0 ? CH : 0;
+  // the chunk buffers exist with children, and also without them when the
+  // parents' value fragments are not held in LDS (they then carry the staged
+  // passes' values)
+  const int nCBbuf = (P > 0 || !values_lds) ? NCB : 0;
   frag_t* sCC = (frag_t*)(sPV + (values_lds ? nblkP * FV : 0));       // [NCB*FA]
-  pvfrag_t* sCV = (pvfrag_t*)(sCC + nCB * FA);                        // [NCB*FV]
-  float* sNp = (float*)(sCV + nCB * FV);                              // [M0p] counts
+  pvfrag_t* sCV = (pvfrag_t*)(sCC + nCBbuf * FA);                     // [NCB*FV]
+  float* sNp = (float*)(sCV + nCBbuf * FV);                           // [M0p] counts
   float* sNc = sNp + M0p;                                             // [CH]
   float* sBp = sNc + nCH;                                             // [M0p] 0 or -inf (empty)
   float* sBc = sBp + M0p;                                             // [CH]
@@ -536,16 +540,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     if (next >= 0) stage_pass(next);
   };
   if constexpr (!parents_lds) stage_pass(0);
-  // Parents' value fragments that are not held in LDS: with children to
-  // refine, the first pass's value products read them from the two child
-  // buffers (idle until the children, each exactly one 64-parent pass of
-  // value fragments in size), shared by the workgroup's waves, instead of
-  // every wave reading them from L2.  Pass pt uses buffer pt % 2; the copy
+  // Parents' value fragments that are not held in LDS: the first pass's value
+  // products read them from the two chunk buffers (idle until the children,
+  // each exactly one 64-parent pass of value fragments in size), shared by
+  // the workgroup's waves, instead of every wave reading them from L2.  Pass pt uses buffer pt % 2; the copy
   // of pass pt + 1 is issued right after pass pt's opening barrier (every
   // wave is then done with pass pt - 1, the buffer's last user) and waited
   // for by pass pt + 1's opening wait and barrier; only pass 0's own copy
   // needs a wait of its own.
-  const bool vstage = !values_lds && nCB > 0;
+  constexpr bool vstage = !values_lds;
   pvfrag_t* const vbuf[2] = {sCV, (pvfrag_t*)sCC};
   auto stage_values = [&](int pt2) {
     pvfrag_t* dst = vbuf[pt2 & 1];
@@ -1417,9 +1420,10 @@ size_t attention_smem_bytes(int dtype, int d, int M0, int C, int P, int block_q,
   const size_t CH = d == 64 ? AttnTraits<64>::kChunkRows : AttnTraits<128>::kChunkRows;
   (void)C;
   const size_t ch = P > 0 ? CH : 0;
+  const bool values_lds = M0p <= 64 || (d == 64 && M0p <= 256);
   size_t b = (M0p <= 64 ? M0p : 64) * d * es;  // parents' codeword fragments (all, or one 64-parent pass)
-  if (M0p <= 64 || (d == 64 && M0p <= 256)) b += M0p * d * es;  // parents' value fragments (else read from L2)
-  b += 2 * ch * d * es;                       // chunk codeword and value fragments
+  if (values_lds) b += M0p * d * es;         // parents' value fragments (else staged per pass)
+  b += 2 * (P > 0 || !values_lds ? CH : 0) * d * es;  // chunk codeword and value fragments
   b += 2 * (M0p + ch) * 4;                    // counts and biases
   if (P > 0 || importance) b += M0p * 4 * 4;           // importance partials
   b += nw * (size_t)(P > 0 ? P : 1) * 4 + 48; // selections, flags, keys per pass
