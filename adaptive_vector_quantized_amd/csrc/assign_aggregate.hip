@@ -175,8 +175,23 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int ql = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.y, h = bh % H;
-  const int cstart = blockIdx.x * chunk;
+  // the chunks of one (batch, head) on one XCD when possible (consecutive
+  // workgroup ids go to the XCDs round robin)
+  int bh, ci;
+  {
+    const int nch = (N + chunk - 1) / chunk;
+    const int L = blockIdx.x;
+    const int BH = gridDim.x / nch;
+    if ((BH & 7) == 0) {
+      bh = (L / (8 * nch)) * 8 + (L & 7);
+      ci = (L >> 3) % nch;
+    } else {
+      bh = L / nch;
+      ci = L % nch;
+    }
+  }
+  const int h = bh % H;
+  const int cstart = ci * chunk;
   const int nval = min(chunk, N - cstart);
   const in_t* cbh = cb + (int64_t)h * Mt * D;
   const in_t* Kb = K + (int64_t)bh * N * D;
@@ -628,7 +643,7 @@ static hipError_t launch_assign_t(const void* K, const void* V, const void* cb, 
   auto kern = assign_aggregate_kernel<T, D, W, PL>;
   hipError_t e = raise_lds_limit((const void*)kern, L.total);
   if (e != hipSuccess) return e;
-  dim3 grid((N + Sh::kChunk - 1) / Sh::kChunk, BH);
+  dim3 grid((unsigned)(((N + Sh::kChunk - 1) / Sh::kChunk) * BH));
   hipLaunchKernelGGL(kern, grid, dim3(256), L.total, st, (const typename T::in_t*)K, (const typename T::in_t*)V,
                      (const typename T::in_t*)cb, H, N, M0, C, L, vsum, counts, assign, ksum);
   return hipGetLastError();
