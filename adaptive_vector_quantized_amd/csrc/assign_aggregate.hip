@@ -207,15 +207,30 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   }
   for (int i = tid; i < NB; i += 256) sHist[i] = 0;
   lds_barrier();
-  for (int i = tid; i < M0p * 4; i += 256) {  // 4 lanes per row; M0p * 4 is a multiple of 64
-    const int row = i >> 2, q = i & 3;
-    const in_t* pr = PL ? sPar + row * LDP + q * (D / 4) : cbh + (int64_t)(row < M0 ? row : 0) * D + q * (D / 4);
-    float acc = 0.0f;
+  // 4 lanes per row (M0p * 4 is a multiple of 64, so whole waves take part);
+  // rows read from L2 are requested NI at a time before any is summed, so a
+  // workgroup waits for them about once per NI rows instead of once each
+  constexpr int NI = PL ? 1 : (E == 8 ? 4 : 1);
+  constexpr int QF = D / 4 / E;  // fragments per row quarter
+  for (int i0 = tid; i0 < M0p * 4; i0 += 256 * NI) {
+    frag_t v[NI][QF];
 #pragma unroll
-    for (int t = 0; t < D / 4; t += E) acc = frag_sumsq<T>(*(const frag_t*)(pr + t), acc);
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    if (q == 0) sNorm[row] = row < M0 ? acc : INFINITY;
+    for (int n = 0; n < NI; ++n) {
+      const int i = i0 + 256 * n, row = min(i >> 2, M0p - 1), q = i & 3;
+      const in_t* pr = PL ? sPar + row * LDP + q * (D / 4) : cbh + (int64_t)(row < M0 ? row : 0) * D + q * (D / 4);
+#pragma unroll
+      for (int t = 0; t < QF; ++t) v[n][t] = *(const frag_t*)(pr + t * E);
+    }
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int i = i0 + 256 * n, row = i >> 2, q = i & 3;
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < QF; ++t) acc = frag_sumsq<T>(v[n][t], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (q == 0 && row < M0p) sNorm[row] = row < M0 ? acc : INFINITY;
+    }
   }
   lds_barrier();
 
