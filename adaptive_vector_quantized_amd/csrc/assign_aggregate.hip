@@ -64,16 +64,19 @@ __device__ __forceinline__ R buf_load(__amdgpu_buffer_rsrc_t r, int voff, int so
 }
 constexpr int kBufWord3 = 0x00020000;
 
+// acc + the squared norm of one fragment (bf16 pairs on v_dot2: the products
+// are exact in fp32)
 template <class T>
 __device__ __forceinline__ float frag_sumsq(typename T::frag_t v, float acc) {
   if constexpr (T::E == 1) {
     const float x = T::to_f32(v);
     return fmaf(x, x, acc);
   } else {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 #pragma unroll
-    for (int j = 0; j < T::E; ++j) {
-      const float x = T::to_f32(v[j]);
-      acc = fmaf(x, x, acc);
+    for (int j = 0; j < T::E / 2; ++j) {
+      const bf16x2 x = {v[2 * j], v[2 * j + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
     }
     return acc;
   }
@@ -370,18 +373,28 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
         const int sl = idx[g] - blk * S;
         if (sl >= 0 && sl < S && (sl & 1) == hh) {
           const int gg = sl >> 1;
+          // the norms of the W rows this lane's registers gg * W .. hold: rows
+          // row_of(gg * W + c, hh), four consecutive rows per quad of c, all
+          // read before any is used
+          float nr[W];
+#pragma unroll
+          for (int q = 0; q < W / 4; ++q) {
+            const f32x4 n4 = *(const f32x4*)(cn + 2 * gg * W + 8 * q + 4 * hh);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) nr[4 * q + u] = n4[u];
+          }
           float dmin = INFINITY;
           int cmin = -1;
 #pragma unroll
           for (int c = 0; c < W; ++c) {
-            if (c < C) {
-              float v = g ? c1[c] : c0[c];
-              int r = c;
+            float v = g ? c1[c] : c0[c];
 #pragma unroll
-              for (int gi = 1; gi < 16 / W; ++gi)
-                if (gg == gi) { v = g ? c1[gi * W + c] : c0[gi * W + c]; r = gi * W + c; }
-              const float dist = cn[row_of(r, hh)] - 2.0f * v;
-              if (dist < dmin) { dmin = dist; cmin = c; }
+            for (int gi = 1; gi < 16 / W; ++gi)
+              if (gg == gi) v = g ? c1[gi * W + c] : c0[gi * W + c];
+            const float dist = nr[c] - 2.0f * v;
+            if (c < C && dist < dmin) {  // children past C are padding rows
+              dmin = dist;
+              cmin = c;
             }
           }
           dch[g] = dmin;
