@@ -623,10 +623,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         for (int r = 0; r < 16; ++r) tm = fmaxf(tm, lg[b][r]);
       tm = xhalf_max(tm) * sl2;
       if (tm > m + kLazy) {
-        const float f = fast_exp2(m - tm);
-        zp *= f;
+        if (pt > 0) {  // (the first pass finds the accumulators still zero)
+          const float f = fast_exp2(m - tm);
+          zp *= f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) xacc[db] *= f;
+          for (int db = 0; db < DB; ++db) xacc[db] *= f;
+        }
         m = tm;
       }
 #pragma unroll
@@ -686,53 +688,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     // importance (Eq. 7) and top-P (Alg. 2, the parent choice)
     if (need_imp) {
       const float rz = qv ? 1.0f / xhalf_sum(zp) : 0.0f;
-      for (int pt = 0; pt < ((approx && !parents_lds) ? 0 : nPT); ++pt) {  // (formed in the pass loop)
-        const int j0 = pt * 64;
+      if constexpr (parents_lds) {
+        // one pass (M0 <= 64): its weights are still in registers; the count
+        // n_j of Eq. 7 is a factor of the whole sum over the tile's queries,
+        // applied once after the reduction
         float t[32];
-        if constexpr (parents_lds) {  // one pass (M0 <= 64): its weights are still in registers
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * rz;
-        } else {
-          // second pass with the final stabiliser and denominator (exact Z of Eq. 7)
+          for (int r = 0; r < 16; ++r) t[b * 16 + r] = lg[b][r] * rz;
+        rs_half32(t, lane);
+        const int j = 32 * (ql >> 4) + row_of(ql & 15, hh);
+        if (j < M0) sW[j * 4 + wave] = t[0] * sNp[32 * (ql >> 4) + col_of(ql & 15, hh)];
+      } else if (!approx) {
+        // Second pass over the parents with the final stabiliser and
+        // denominator (the exact Z of Eq. 7).  Its logits are formed
+        // untransposed (the MFMA operands swapped: rows = this wave's queries,
+        // columns = parents), so that a lane holds one parent for 16 queries
+        // and the sum over the wave's queries is a sum over its registers and
+        // the two lane halves.  Each register's query (row row_of(r, hh))
+        // brings its stabiliser and 1/z, read once per tile from a table of
+        // the wave's 32 queries in its own output-staging rows (idle until the
+        // output).
+        if (hh == 0) {
+          yw[ql] = m;
+          yw[32 + ql] = rz;
+        }
+        float mr[16], rr[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 a = *(const f32x4*)(yw + 8 * q + 4 * hh);
+          const f32x4 c = *(const f32x4*)(yw + 32 + 8 * q + 4 * hh);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            mr[4 * q + u] = a[u];
+            rr[4 * q + u] = c[u];
+          }
+        }
+        // this lane's parent column in the count and bias arrays (stored by
+        // staged value column)
+        const int ccol = col_of(r_of_row(ql), h_of_row(ql));
+        for (int pt = 0; pt < nPT; ++pt) {
+          const int j0 = pt * 64;
           wait_pass();
           f32x16 l2[2];
           const bool pass_masked = !all_parents || j0 + 64 > M0;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            l2[b] = zero16();
-            if (pass_masked) {  // as in the first pass: empty parents and padding rows at -inf
-              const f32x4* bp = (const f32x4*)(sBp + j0 + b * 32 + 8 * hh);
+            // empty parents and padding columns at -inf, as in the first pass
+            const float bj = pass_masked ? sBp[j0 + b * 32 + ccol] : 0.0f;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const f32x4 b4 = bp[(q >> 1) * 4 + (q & 1)];
+            for (int r = 0; r < 16; ++r) l2[b][r] = bj;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) l2[b][q * 4 + u] = b4[u];
-              }
-            }
-#pragma unroll
-            for (int s = 0; s < KS; ++s) l2[b] = T::mma_in(sPC[(b * KS + s) * 64 + lane], qf[s], l2[b]);
+            for (int s = 0; s < KS; ++s) l2[b] = T::mma_in(qf[s], sPC[(b * KS + s) * 64 + lane], l2[b]);
           }
           release_pass(pt + 1 < nPT ? pt + 1 : tile + 1 < tile1 ? 0 : -1);
           // the stabiliser bounds every logit of a parent with keys (exp2 of
           // at most the lazy margin) and the others are -inf: every term is
           // finite, and exactly 0 for a parent without keys
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int b = 0; b < 2; ++b) {
+            float acc = 0.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float n = sNp[j0 + b * 32 + col_of(r, hh)];
-              t[b * 16 + r] = fast_exp2(fmaf(l2[b][r], sl2, -m)) * (n * rz);
-            }
+            for (int r = 0; r < 16; ++r) acc = fmaf(fast_exp2(fmaf(l2[b][r], sl2, -mr[r])), rr[r], acc);
+            acc = xhalf_sum(acc);
+            const int j = j0 + b * 32 + ql;
+            if (hh == 0 && j < M0) sW[j * 4 + wave] = acc * sNp[j0 + b * 32 + ccol];
+          }
         }
-        // one pass: the count n_j of Eq. 7 is a factor of the whole sum over
-        // the tile's queries, applied once after the reduction (the second
-        // pass has it in every term)
-        rs_half32(t, lane);
-        const int j = j0 + 32 * (ql >> 4) + row_of(ql & 15, hh);
-        const float nj = parents_lds ? sNp[32 * (ql >> 4) + col_of(ql & 15, hh)] : 1.0f;
-        if (j < M0) sW[j * 4 + wave] = t[0] * nj;
       }
       lds_barrier();
       // every wave forms the totals and its own copy of the selection; the
