@@ -61,7 +61,7 @@ CALLS = {
                                    ["adaptive_vector_quantized_amd/csrc/assign_aggregate.hip",
                                     "adaptive_vector_quantized_amd/csrc/avq_device.h"]),
     "avq_attention_prepare": ("attention_prep_kernel", _ATTN_SRC),
-    "avq_attention_fwd_prepared": ("attention_kernel (or attention_pipe_kernel)", _ATTN_SRC),
+    "avq_attention_fwd_prepared": ("attention_kernel", _ATTN_SRC),
     "avq_attention_fwd": ("attention_prep_kernel + attention_kernel", _ATTN_SRC),
 }
 
@@ -72,6 +72,26 @@ def source_hash(call: str) -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def attention_launches(cfg, P):
+    """(preparation kernels, attention kernel) the attention calls launch on
+    this workload, by the launcher's rules in csrc/attention.hip: the value
+    fragments come from attention_prep_kernel, after a first pass of
+    attention_absmax_kernel when the prep blocks' repeated reads of a head's
+    value sums would pass 8 MiB (bf16 only); the pipelined kernel serves bf16,
+    d = 64, at most 64 parents (one LDS-resident pass) and P > 0."""
+    bf16 = cfg.dtype == "bf16"
+    E = 8 if bf16 else 1
+    W = 8 if cfg.C <= 8 else 16
+    M0p = (cfg.M0 + 63) // 64 * 64
+    nF = (M0p // 32) * (16 // E) * 2 * cfg.d + (cfg.M0 * (W // E) * cfg.d if cfg.C > 0 else 0)
+    parts = max(8, -(-nF // (512 * 2)))
+    head_bytes = cfg.M0 * (1 + cfg.C) * cfg.d * 4
+    prep = ("attention_absmax_kernel + attention_prep_kernel" if bf16 and parts * head_bytes > (8 << 20)
+            else "attention_prep_kernel")
+    kern = "attention_pipe_kernel" if bf16 and cfg.d == 64 and M0p <= 64 and P > 0 else "attention_kernel"
+    return prep, kern
 
 
 def algorithmic(cfg, P):
@@ -503,13 +523,16 @@ def main():
     value = tokens / (wall / args.steps) / 1e6
     alg = algorithmic(cfg, P)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_FP32_PEAK_TFLOPS
+    prep_k, attn_k = attention_launches(cfg, P)
+    launches = {"avq_attention_prepare": prep_k, "avq_attention_fwd_prepared": attn_k,
+                "avq_attention_fwd": f"{prep_k} + {attn_k}"}
     units = {}
     for j, name in enumerate(st_[0].names):
         b, f = alg[name]
         t = per[:, j]
         avg = float(t.mean())
         units[name] = {
-            "launches": CALLS[name][0],
+            "launches": launches.get(name, CALLS[name][0]),
             "avg_us": avg * 1e6, "median_us": float(np.median(t)) * 1e6,
             "algorithmic_bytes": b, "algorithmic_flops": f,
             "GBps": b / avg / 1e9, "hbm_frac": b / avg / 1e9 / HBM_PEAK_GBS,
@@ -540,7 +563,7 @@ def main():
             "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "parallelism": "single GPU",
         },
         "roofline": {
-            "call": dom, "kernel": CALLS[dom][0],
+            "call": dom, "kernel": units[dom]["launches"],
             "bound": "hbm", "achieved": round(kd["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kd["hbm_frac"], 4), "traffic": traffic,
             "mfma": {"achieved": round(kd["TFLOPs"], 2), "peak": mfma_peak, "unit": "TFLOP/s",

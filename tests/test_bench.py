@@ -60,3 +60,23 @@ def test_multi_gpu_request_exits():
 
 def test_metric_is_the_headline():
     assert bench.METRIC.startswith("AVQ fwd Mtokens/s at N=16384,H=16,d=64,M0=64,C=8,P=16")
+
+
+def test_dominant_kernel_names():
+    """The roofline's kernel follows the launcher's choice: the pipelined
+    kernel for the bf16 d = 64 shapes with one parent pass and children to
+    refine, the general kernel otherwise; large heads get the split maximum
+    before the preparation (their traces in profiles/ show the same names)."""
+    C = gen.CONFIGS
+    assert bench.attention_launches(C["grid128"], 16) == ("attention_prep_kernel", "attention_pipe_kernel")
+    assert bench.attention_launches(C["sweep"], 0)[1] == "attention_kernel"
+    assert bench.attention_launches(C["sweep"], 64)[1] == "attention_pipe_kernel"
+    assert bench.attention_launches(C["grid256"], 32) == ("attention_absmax_kernel + attention_prep_kernel",
+                                                          "attention_kernel")
+    assert bench.attention_launches(C["flat512"], 0) == ("attention_prep_kernel", "attention_kernel")
+    assert bench.attention_launches(C["tiny"], 4)[1] == "attention_kernel"  # fp32
+    with open(os.path.join(ROOT, "profiles", "kernels_grid128_stats.txt")) as f:
+        assert "attention_pipe_kernel" in f.read()
+    with open(os.path.join(ROOT, "profiles", "kernels_grid256_stats.txt")) as f:
+        text = f.read()
+        assert "attention_absmax_kernel" in text and "avq::attention_kernel<" in text
