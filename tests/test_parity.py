@@ -278,6 +278,20 @@ def _full_size(name, P=None):
     _full_check(data, P)
 
 
+@pytest.mark.parametrize("over", [
+    dict(H=8, N=4096 + 1000 + 7, grid=None),                         # pipelined kernel, bf16
+    dict(H=8, N=4096 + 1000 + 7, grid=None, dtype="f32", P=8),       # fp32
+    dict(d=128, M0=256, P=32, H=8, N=3000 + 11, grid=None),          # two-pass, parents from L2
+])
+def test_heads_per_xcd_ragged(over):
+    """B*H a multiple of 8, so that both kernels number the workgroups of one
+    (batch, head) onto one XCD, with a ragged sequence end (a partial key chunk
+    and a partial query tile per head): every assignment, count and value sum,
+    and every tile's importances, top-P and Y."""
+    data = _data("grid64", **over)
+    _full_check(data, data["cfg"].P)
+
+
 @pytest.mark.timeout(600)
 def test_full_size_grid128():
     """The headline workload (B2 H16 N16384 d64 M0 64 C8 P16, 128-query tiles)
