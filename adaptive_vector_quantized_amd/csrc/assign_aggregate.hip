@@ -201,9 +201,33 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   const in_t* Vb = V + (int64_t)bh * N * D;
 
   // ---- stage parents, clear the histogram, parent norms -----------------
+  // With all parents in LDS, the first 32 keys of this wave's first step are
+  // requested right after the first round of parent loads (straight into
+  // their operand registers): they stream in during the set-up instead of
+  // after it, and the wait for the parents (the counter retires in order)
+  // does not wait for them.
+  frag_t kf0[KS];
   if constexpr (PL) {
-    for (int i = tid; i < M0p * (D / E); i += 256) {
-      const int row = i / (D / E), col = (i % (D / E)) * E;
+    constexpr int NF = D / E;  // fragments per parent row
+    const int nfr = M0p * NF;  // a multiple of 256: every thread owns one or more whole rounds
+    // the first two rounds, both loads unconditional (a single round repeats
+    // the first), so that neither is moved to its store
+    const int i1 = nfr > 256 ? tid + 256 : tid;
+    // (padding rows past M0 repeat row M0 - 1: their norm is +inf, never chosen)
+    const frag_t pre0 = *(const frag_t*)(cbh + (int64_t)min(tid / NF, M0 - 1) * D + (tid % NF) * E);
+    const frag_t pre1 = *(const frag_t*)(cbh + (int64_t)min(i1 / NF, M0 - 1) * D + (i1 % NF) * E);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const int kl = wave * KPW + ql;  // chunk-relative key of this lane
+      const in_t* kp = Kb + (int64_t)(kl < nval ? cstart + kl : cstart) * D + E * hh;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf0[s] = *(const frag_t*)(kp + s * 2 * E);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    *(frag_t*)(sPar + (tid / NF) * LDP + (tid % NF) * E) = pre0;
+    *(frag_t*)(sPar + (i1 / NF) * LDP + (i1 % NF) * E) = pre1;
+    for (int i = tid + 512; i < M0p * NF; i += 256) {
+      const int row = i / NF, col = (i % NF) * E;
       const int src = row < M0 ? row : 0;
       *(frag_t*)(sPar + row * LDP + col) = *(const frag_t*)(cbh + (int64_t)src * D + col);
     }
@@ -272,6 +296,11 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     for (int g = 0; g < 2; ++g) {
       key[g] = cstart + kloc + g * 32 + ql;
       kval[g] = it + g * 32 + ql < KPW && kloc + g * 32 + ql < nval;
+      if (PL && g == 0 && it == 0) {  // requested during the set-up
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kf[0][s] = kf0[s];
+        continue;
+      }
       const in_t* kp = Kb + (int64_t)(kval[g] ? key[g] : cstart) * D + E * hh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) kf[g][s] = *(const frag_t*)(kp + s * 2 * E);
