@@ -206,7 +206,16 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // their operand registers): they stream in during the set-up instead of
   // after it, and the wait for the parents (the counter retires in order)
   // does not wait for them.
+  // (with parents read from L2 only where the registers allow: at four waves
+  // per SIMD the early keys would spill)
+  constexpr bool kEarlyKeys = PL || Sh::kWavesL2 < 4;
   frag_t kf0[KS];
+  auto request_first_keys = [&]() {
+    const int kl = wave * KPW + ql;  // chunk-relative key of this lane
+    const in_t* kp = Kb + (int64_t)(kl < nval ? cstart + kl : cstart) * D + E * hh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf0[s] = *(const frag_t*)(kp + s * 2 * E);
+  };
   if constexpr (PL) {
     constexpr int NF = D / E;  // fragments per parent row
     const int nfr = M0p * NF;  // a multiple of 256: every thread owns one or more whole rounds
@@ -217,12 +226,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     const frag_t pre0 = *(const frag_t*)(cbh + (int64_t)min(tid / NF, M0 - 1) * D + (tid % NF) * E);
     const frag_t pre1 = *(const frag_t*)(cbh + (int64_t)min(i1 / NF, M0 - 1) * D + (i1 % NF) * E);
     __builtin_amdgcn_sched_barrier(0);
-    {
-      const int kl = wave * KPW + ql;  // chunk-relative key of this lane
-      const in_t* kp = Kb + (int64_t)(kl < nval ? cstart + kl : cstart) * D + E * hh;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf0[s] = *(const frag_t*)(kp + s * 2 * E);
-    }
+    request_first_keys();
     __builtin_amdgcn_sched_barrier(0);
     *(frag_t*)(sPar + (tid / NF) * LDP + (tid % NF) * E) = pre0;
     *(frag_t*)(sPar + (i1 / NF) * LDP + (i1 % NF) * E) = pre1;
@@ -239,6 +243,9 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // workgroup waits for them about once per NI rows instead of once each
   constexpr int NI = PL ? 1 : (E == 8 ? 4 : 1);
   constexpr int QF = D / 4 / E;  // fragments per row quarter
+  // (parents read from L2: the first keys are requested right after the
+  // first round of these loads, as the other instantiation does after its
+  // parent loads; every thread takes part in the first round, M0p >= 64)
   for (int i0 = tid; i0 < M0p * 4; i0 += 256 * NI) {
     frag_t v[NI][QF];
 #pragma unroll
@@ -247,6 +254,13 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
       const in_t* pr = PL ? sPar + row * LDP + q * (D / 4) : cbh + (int64_t)(row < M0 ? row : 0) * D + q * (D / 4);
 #pragma unroll
       for (int t = 0; t < QF; ++t) v[n][t] = *(const frag_t*)(pr + t * E);
+    }
+    if constexpr (!PL && kEarlyKeys) {
+      if (i0 == tid) {
+        __builtin_amdgcn_sched_barrier(0);
+        request_first_keys();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
     for (int n = 0; n < NI; ++n) {
@@ -258,6 +272,9 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
       acc += __shfl_xor(acc, 2);
       if (q == 0 && row < M0p) sNorm[row] = row < M0 ? acc : INFINITY;
     }
+  }
+  if constexpr (!PL && kEarlyKeys) {
+    if (tid >= M0p * 4) request_first_keys();  // (a thread the loop above skipped)
   }
   lds_barrier();
 
@@ -296,7 +313,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
     for (int g = 0; g < 2; ++g) {
       key[g] = cstart + kloc + g * 32 + ql;
       kval[g] = it + g * 32 + ql < KPW && kloc + g * 32 + ql < nval;
-      if (PL && g == 0 && it == 0) {  // requested during the set-up
+      if (kEarlyKeys && g == 0 && it == 0) {  // requested during the set-up
 #pragma unroll
         for (int s = 0; s < KS; ++s) kf[0][s] = kf0[s];
         continue;
