@@ -201,13 +201,13 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   const in_t* Vb = V + (int64_t)bh * N * D;
 
   // ---- stage parents, clear the histogram, parent norms -----------------
-  // With all parents in LDS, the first 32 keys of this wave's first step are
-  // requested right after the first round of parent loads (straight into
-  // their operand registers): they stream in during the set-up instead of
-  // after it, and the wait for the parents (the counter retires in order)
-  // does not wait for them.
-  // (with parents read from L2 only where the registers allow: at four waves
-  // per SIMD the early keys would spill)
+  // The first 32 keys of this wave's first step are requested right after
+  // the first round of set-up loads (the parents' rows when they are all held
+  // in LDS, else the first round of norm reads), straight into their operand
+  // registers: they stream in during the set-up instead of after it, and the
+  // wait for those loads does not wait for them (the counter retires in
+  // order).  With parents read from L2 at four waves per SIMD the registers
+  // do not allow it (the early keys would spill).
   constexpr bool kEarlyKeys = PL || Sh::kWavesL2 < 4;
   frag_t kf0[KS];
   auto request_first_keys = [&]() {
@@ -243,9 +243,6 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
   // workgroup waits for them about once per NI rows instead of once each
   constexpr int NI = PL ? 1 : (E == 8 ? 4 : 1);
   constexpr int QF = D / 4 / E;  // fragments per row quarter
-  // (parents read from L2: the first keys are requested right after the
-  // first round of these loads, as the other instantiation does after its
-  // parent loads; every thread takes part in the first round, M0p >= 64)
   for (int i0 = tid; i0 < M0p * 4; i0 += 256 * NI) {
     frag_t v[NI][QF];
 #pragma unroll
@@ -256,7 +253,7 @@ assign_aggregate_kernel(const typename T::in_t* __restrict__ K, const typename T
       for (int t = 0; t < QF; ++t) v[n][t] = *(const frag_t*)(pr + t * E);
     }
     if constexpr (!PL && kEarlyKeys) {
-      if (i0 == tid) {
+      if (i0 == tid) {  // the first round (every thread takes part: M0p >= 64 here)
         __builtin_amdgcn_sched_barrier(0);
         request_first_keys();
         __builtin_amdgcn_sched_barrier(0);
