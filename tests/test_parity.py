@@ -279,6 +279,25 @@ def _full_size(name, P=None):
 
 
 @pytest.mark.parametrize("over", [
+    dict(M0=128, C=16, P=8),                    # bf16 d64: parents from L2, values in LDS, 16-row slots
+    dict(M0=300, C=12, P=8),                    # bf16 d64: parents and values from L2, 16-row slots
+    dict(d=128, M0=64, C=16, P=16),             # bf16 d128: one parent pass, 16-row slots
+    dict(d=128, M0=256, C=12, P=16),            # bf16 d128: two-pass, 16-row slots
+    dict(d=128, M0=256, C=3, P=16),             # bf16 d128: 4-row slots in the assignment
+    dict(dtype="f32", M0=64, C=16, P=8),        # fp32 d64: 16-row slots
+    dict(dtype="f32", d=128, M0=128, C=16, P=8),  # fp32 d128: two-pass, 16-row slots
+    dict(dtype="f32", M0=128, C=2, P=8),        # fp32 d64: parents from L2, 4-row slots
+])
+def test_slot_widths_all_paths(over):
+    """The child-slot widths (4, 8 or 16 rows per parent, by C) on the
+    instantiations the other cases do not reach: every data type and head
+    dimension, parents in LDS or read from L2, each with a ragged end; every
+    assignment, count and value sum, every tile's importances, top-P and Y."""
+    data = _data("grid64", H=2, N=1024 + 37, grid=None, **over)
+    _full_check(data, data["cfg"].P)
+
+
+@pytest.mark.parametrize("over", [
     dict(H=8, N=4096 + 1000 + 7, grid=None),                         # pipelined kernel, bf16
     dict(H=8, N=4096 + 1000 + 7, grid=None, dtype="f32", P=8),       # fp32
     dict(d=128, M0=256, P=32, H=8, N=3000 + 11, grid=None),          # two-pass, parents from L2
