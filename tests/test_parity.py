@@ -287,12 +287,25 @@ def _full_size(name, P=None):
     dict(dtype="f32", M0=64, C=16, P=8),        # fp32 d64: 16-row slots
     dict(dtype="f32", d=128, M0=128, C=16, P=8),  # fp32 d128: two-pass, 16-row slots
     dict(dtype="f32", M0=128, C=2, P=8),        # fp32 d64: parents from L2, 4-row slots
+    dict(d=128, M0=16, C=2, P=4),               # bf16 d128: 4-row slots, parents in LDS
+    dict(M0=16, C=12, P=0),                     # bf16 d64: plain VQ pass with 16-row slots
+    dict(dtype="f32", d=128, M0=16, C=2, P=4),  # fp32 d128: one parent pass, 4-row slots
+    dict(dtype="f32", d=128, M0=16, C=12, P=4),  # fp32 d128: one parent pass, 16-row slots
+    dict(dtype="f32", d=128, M0=16, C=8, P=4),  # fp32 d128: one parent pass, 8-row slots
+    dict(dtype="f32", d=128, M0=200, C=2, P=8),  # fp32 d128: parents from L2, 4-row slots
+    dict(dtype="f32", M0=200, C=12, P=8),       # fp32 d64: parents from L2, 16-row slots
+    dict(dtype="f32", M0=256, C=3, P=8),        # fp32 d64: parents from L2, 4-row slots
+    dict(dtype="f32", M0=256, C=8, P=8),        # fp32 d64: parents from L2, 8-row slots
+    dict(dtype="f32", M0=300, C=12, P=8),       # fp32 d64: parents and values from L2, 16-row slots
+    dict(dtype="f32", M0=300, C=2, P=8),        # fp32 d64: parents and values from L2, 8-row slots
 ])
 def test_slot_widths_all_paths(over):
     """The child-slot widths (4, 8 or 16 rows per parent, by C) on the
-    instantiations the other cases do not reach: every data type and head
-    dimension, parents in LDS or read from L2, each with a ragged end; every
-    assignment, count and value sum, every tile's importances, top-P and Y."""
+    instantiations the other cases do not reach: with the rest of the suite,
+    every compiled variant of both kernels (data type, head dimension, slot
+    width, parents in LDS or read from L2) runs under parity.  Each case has a
+    ragged end; every assignment, count and value sum, every tile's
+    importances, top-P and Y."""
     data = _data("grid64", H=2, N=1024 + 37, grid=None, **over)
     _full_check(data, data["cfg"].P)
 
