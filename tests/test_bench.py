@@ -80,3 +80,26 @@ def test_dominant_kernel_names():
     with open(os.path.join(ROOT, "profiles", "kernels_grid256_stats.txt")) as f:
         text = f.read()
         assert "attention_absmax_kernel" in text and "avq::attention_kernel<" in text
+
+
+def test_recorded_bench_lines_parse():
+    """Every recorded bench line under profiles/ is one JSON object (the
+    line bench.py prints and nothing else) naming its metric, unit, dtype,
+    workload and step counts; the headline workload's line also carries the
+    roofline and the CPU baseline."""
+    import glob
+    import json
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "bench_*.json")))
+    assert paths
+    for p in paths:
+        with open(p) as f:
+            lines = [l for l in f.read().splitlines() if l.strip()]
+        assert len(lines) == 1, p
+        rec = json.loads(lines[0])
+        for key in ("metric", "unit", "steps", "warmup", "dtype", "config"):
+            assert key in rec, (p, key)
+    with open(os.path.join(ROOT, "profiles", "bench_grid128.json")) as f:
+        rec = json.load(f)
+    assert rec["metric"] == bench.METRIC and rec["n_gpus"] == 1
+    assert {"bound", "achieved", "peak", "unit", "frac"} <= set(rec["roofline"])
+    assert rec["cpu_baseline"]["kind"] == "oracle"
