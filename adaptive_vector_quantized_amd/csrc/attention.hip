@@ -1274,6 +1274,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
           float acc = cl[bb][g2 * W];
 #pragma unroll
           for (int c = 1; c < W; ++c) acc += cl[bb][g2 * W + c];
+          // formed here, before the rare masking below, so that the unmasked
+          // logits are dead once they are masked in place (formed after the
+          // branch, they stay live across it and the merge copies all 32)
+          asm volatile("" : "+v"(acc));
           sp[bb][g2] = acc;
         }
       float tm = -INFINITY;
