@@ -26,7 +26,9 @@ Prints one JSON line:
                    the launch stream around the call, inside the timed
                    region) against MI355X's 8 TB/s HBM peak, and its
                    algorithmic MFMA flops against the 2.5 PFLOP/s dense bf16
-                   peak; traffic = counter-measured HBM bytes per launch
+                   peak; traffic = counter-measured HBM bytes per launch;
+                   traced = the same fractions at the average duration of
+                   the committed kernel trace of the same source
   units            the same figures for every unit of the step
   cpu_baseline     the CPU oracle on the same workload
 
@@ -127,8 +129,9 @@ def algorithmic(cfg, P):
             "avq_attention_fwd": (k2_bytes, k2_flops)}
 
 
-def load_traffic(call: str, workload: str):
-    """HBM bytes per call from the committed rocprofv3 counter summary, if it
+def load_record(call: str, workload: str):
+    """The committed rocprofv3 record of a call on a workload (HBM bytes per
+    launch from the counter runs; the kernel trace's average duration), if it
     was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", f"{call}_{workload}_traffic.json")
     if not os.path.exists(path):
@@ -137,7 +140,24 @@ def load_traffic(call: str, workload: str):
         rec = json.load(f)
     if rec.get("source_hash") != source_hash(call):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def load_traffic(call: str, workload: str):
+    """HBM bytes per call from the committed counter record, if current."""
+    rec = load_record(call, workload)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def traced_fractions(rec, alg_bytes: float, alg_flops: float, mfma_peak: float):
+    """The roofline fractions of the dominant kernel at the average duration
+    the committed kernel trace of the same source measured (the figure the
+    live HIP-event fractions are checked against), or None."""
+    if rec is None or not rec.get("trace_avg_us"):
+        return None
+    t = rec["trace_avg_us"] * 1e-6
+    return {"avg_us": rec["trace_avg_us"], "frac": round(alg_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(alg_flops / t / 1e12 / mfma_peak, 4), "stats": rec.get("trace_stats")}
 
 
 def _cpu_model() -> str:
@@ -540,7 +560,8 @@ def main():
         }
     dom = max(units, key=lambda k: units[k]["avg_us"])
     kd = units[dom]
-    traffic = load_traffic(dom, cfg.name) if qorder is None else None
+    rec = load_record(dom, cfg.name) if qorder is None else None
+    traffic = None if rec is None else rec.get("bytes_per_launch")
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -568,6 +589,7 @@ def main():
             "frac": round(kd["hbm_frac"], 4), "traffic": traffic,
             "mfma": {"achieved": round(kd["TFLOPs"], 2), "peak": mfma_peak, "unit": "TFLOP/s",
                      "frac": round(kd["mfma_frac"], 4)},
+            "traced": traced_fractions(rec, kd["algorithmic_bytes"], kd["algorithmic_flops"], mfma_peak),
         },
         "units": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                   for k, v in units.items()},

@@ -103,3 +103,30 @@ def test_recorded_bench_lines_parse():
     assert rec["metric"] == bench.METRIC and rec["n_gpus"] == 1
     assert {"bound", "achieved", "peak", "unit", "frac"} <= set(rec["roofline"])
     assert rec["cpu_baseline"]["kind"] == "oracle"
+
+
+def test_traced_roofline_record():
+    """The committed record of the dominant call on the headline workload is
+    current (taken on the kernel source as it stands) and carries the kernel
+    trace's average duration, which the bench line turns into the traced
+    roofline fractions beside the live ones; a record of another source is
+    not used."""
+    import json
+    cfg = gen.CONFIGS["grid128"]
+    rec = bench.load_record("avq_attention_fwd_prepared", "grid128")
+    assert rec is not None and rec["trace_avg_us"] > 0
+    with open(os.path.join(ROOT, rec["trace_stats"])) as f:
+        assert any(rec["kernel"] in l and f"{rec['trace_avg_us']:.3f}" in l for l in f)
+    b, fl = bench.algorithmic(cfg, cfg.P)["avq_attention_fwd_prepared"]
+    tr = bench.traced_fractions(rec, b, fl, 2500.0)
+    assert abs(tr["frac"] - b / (rec["trace_avg_us"] * 1e-6) / 8e12) < 1e-4
+    assert abs(tr["mfma_frac"] - fl / (rec["trace_avg_us"] * 1e-6) / 2.5e15) < 1e-4
+    assert bench.traced_fractions(None, b, fl, 2500.0) is None
+    stale = dict(rec, source_hash="0" * 16)
+    path = os.path.join(ROOT, "profiles", "avq_attention_fwd_prepared_stale-check_traffic.json")
+    try:
+        with open(path, "w") as f:
+            json.dump(stale, f)
+        assert bench.load_record("avq_attention_fwd_prepared", "stale-check") is None
+    finally:
+        os.remove(path)
