@@ -105,13 +105,12 @@ def test_recorded_bench_lines_parse():
     assert rec["cpu_baseline"]["kind"] == "oracle"
 
 
-def test_traced_roofline_record():
+def test_traced_roofline_record(monkeypatch):
     """The committed record of the dominant call on the headline workload is
     current (taken on the kernel source as it stands) and carries the kernel
     trace's average duration, which the bench line turns into the traced
     roofline fractions beside the live ones; a record of another source is
     not used."""
-    import json
     cfg = gen.CONFIGS["grid128"]
     rec = bench.load_record("avq_attention_fwd_prepared", "grid128")
     assert rec is not None and rec["trace_avg_us"] > 0
@@ -122,11 +121,7 @@ def test_traced_roofline_record():
     assert abs(tr["frac"] - b / (rec["trace_avg_us"] * 1e-6) / 8e12) < 1e-4
     assert abs(tr["mfma_frac"] - fl / (rec["trace_avg_us"] * 1e-6) / 2.5e15) < 1e-4
     assert bench.traced_fractions(None, b, fl, 2500.0) is None
-    stale = dict(rec, source_hash="0" * 16)
-    path = os.path.join(ROOT, "profiles", "avq_attention_fwd_prepared_stale-check_traffic.json")
-    try:
-        with open(path, "w") as f:
-            json.dump(stale, f)
-        assert bench.load_record("avq_attention_fwd_prepared", "stale-check") is None
-    finally:
-        os.remove(path)
+    # once the kernel sources change, the record no longer counts
+    monkeypatch.setattr(bench, "source_hash", lambda call: "0" * 16)
+    assert bench.load_record("avq_attention_fwd_prepared", "grid128") is None
+    assert bench.load_traffic("avq_attention_fwd_prepared", "grid128") is None
