@@ -71,6 +71,21 @@ def test_tiny_bf16():
     _full_check(_data("tiny", dtype="bf16"), 4)
 
 
+@pytest.mark.parametrize("M0,C,P,dtype", [
+    (1, 1, 1, "bf16"),    # one parent with one child, refined (the pipelined kernel)
+    (1, 4, 0, "f32"),     # one parent, plain VQ attention
+    (2, 16, 2, "bf16"),   # two parents, 16-row child slots, both refined
+    (3, 1, 2, "bf16"),    # three parents, 4-row child slots
+    (3, 8, 3, "f32"),     # every parent refined
+    (33, 4, 5, "bf16"),   # one row past a 32-row block of parents
+])
+def test_few_parents(M0, C, P, dtype):
+    """Codebooks of one to a few parents: the parent rows are padded to whole
+    MFMA blocks (norm +inf in the assignment, count 0 and logit -inf in the
+    attention), and most child slots of a tile are empty (slots past P)."""
+    _full_check(_data("tiny", H=2, N=1000, M0=M0, C=C, P=P, dtype=dtype), P)
+
+
 @pytest.mark.parametrize("dtype,P", [("f32", 4), ("f32", 12), ("bf16", 12)])
 def test_sparse_occupancy(dtype, P):
     """Keys crowd into a few parents (Zipf s = 4 over 16 parents): most parents
